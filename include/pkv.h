@@ -1,0 +1,255 @@
+/*
+ * pkv.h -- paged-KV chunk attention for one MI355X (gfx950).
+ *
+ * The operations follow "Out of the Memory Barrier: A Highly Memory Efficient
+ * Training System for LLMs with Million-Token Contexts" as summarised on
+ * gist.science (de: sections 2.A-2.D; fr: technical summary 2.B-2.D;
+ * nl: "Methodologie") and sciencestack.ai (abstract, Figures 3 and 5):
+ *   - the sequence is processed in query chunks; each chunk's K/V are appended
+ *     to a paged cache made of fixed-size pages, without reallocation
+ *     (de 2.B, "Paged Memory Management");
+ *   - custom kernels run attention forward and backward directly on the paged
+ *     cache; the cache is not an autograd activation, and the gradients of
+ *     the cached K/V are accumulated in place with atomic adds into a paged
+ *     gradient pool (de 2.B; fr 2.B; sciencestack Figure 3);
+ *   - activations are recomputed in the backward (de 2.A), so the backward
+ *     takes the forward's log-sum-exp and rebuilds the probabilities;
+ *   - for dense-attention models, each query page attends only to the top-K
+ *     key pages scored through one representative vector per page
+ *     (de 2.D; nl "Methodologie"; sciencestack Figure 5);
+ *   - the cache and its gradients can live in pinned host memory and move
+ *     asynchronously on a side stream while compute runs (de 2.C; nl
+ *     "Methodologie", asynchronous CPU offloading).
+ *
+ * Conventions shared by every call
+ *   Hq query heads, Hkv KV heads (Hq % Hkv == 0, G = Hq / Hkv; query head h
+ *   uses KV head h / G), head dim d, page size P tokens.  Positions are
+ *   absolute token indices.  Query/output tensors of a chunk are
+ *   [n_q][Hq][d] row-major; K/V handed to append are [n_tok][Hkv][d].
+ *   The log-sum-exp is [Hq][n_q] fp32, natural log.
+ *   A query at absolute position t attends to keys s <= t (every earlier page
+ *   plus the causal part of its own chunk); in sparse mode additionally only
+ *   to keys whose page is in the selection of t's query page.
+ *
+ *   Device pointers are raw HIP device addresses (for example
+ *   torch.Tensor.data_ptr()).  They stay owned by the caller and must remain
+ *   valid until the enqueued work has completed; the library never keeps
+ *   them after a call returns.  Every call that takes a stream enqueues its
+ *   work on that stream and returns without synchronising the device, unless
+ *   stated otherwise.
+ *
+ * Errors
+ *   Argument and state checks run on the host before anything is enqueued;
+ *   a failing check returns a non-zero pkv_status and enqueues nothing.
+ *   A failing HIP call returns PKV_EHIP.  pkv_last_error() returns a
+ *   thread-local description of the last non-OK status.  Faults that happen
+ *   inside kernels surface at the caller's next stream synchronisation.
+ *   No C++ exception crosses this interface.  A pool is not thread-safe:
+ *   drive each pool from one host thread.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,      /* bad argument (null pointer, size, alignment, range) */
+  PKV_ENOMEM = 2,      /* device or pinned host allocation failed / over budget */
+  PKV_ECAPACITY = 3,   /* a page table entry or an append exceeds the pool */
+  PKV_ESTATE = 4,      /* call out of order (e.g. attention past the appended length) */
+  PKV_EHIP = 5,        /* a HIP runtime call failed */
+  PKV_EUNSUPPORTED = 6 /* shape or dtype combination without a kernel */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* What pkv_read_pages exports. */
+typedef enum { PKV_K = 0, PKV_V = 1, PKV_DK = 2, PKV_DV = 3, PKV_REPS = 4 } pkv_what;
+
+typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
+
+/*
+ * Pool descriptor.  One pool holds, for each of n_layers layers and each KV
+ * head, n_slots page slots of P x d elements for K, V, dK and dV, one page
+ * table (logical page -> slot) and one representative vector per slot.
+ *
+ *   kv_dtype     storage type of K/V and of the query/output tensors of the
+ *                attention calls (PKV_F32 or PKV_BF16).  Gradients (dK, dV,
+ *                dQ) are always fp32 on the device.
+ *   page_size    tokens per page.  PKV_F32 needs page_size % 16 == 0;
+ *                PKV_BF16 needs page_size % 128 == 0.
+ *   head_dim     PKV_F32: 64 or 128.  PKV_BF16: 128.
+ *   max_logical_pages  pages per layer per KV head (context / page_size).
+ *   n_slots      slots per layer per KV head (>= max_logical_pages).
+ *   host_tier    0: all pools in HBM.  1: K, V, dK, dV of every layer live in
+ *                pinned host memory (K/V in kv_dtype, gradients in
+ *                host_grad_dtype) and HBM holds a window of two layers that
+ *                pkv_prefetch_pages fills; representatives and page tables
+ *                stay in HBM.
+ *   host_grad_dtype  host-tier gradient storage (PKV_F32 or PKV_BF16).
+ *   device_budget_bytes  host-tier only: cap on the library's HBM use; pool
+ *                creation fails with PKV_ENOMEM if the window does not fit
+ *                (0 = no cap).
+ */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_logical_pages;
+  int32_t n_slots;
+  int32_t kv_dtype;        /* pkv_dtype */
+  int32_t host_tier;       /* 0 or 1 */
+  int32_t host_grad_dtype; /* pkv_dtype, host-tier only */
+  int32_t reserved;
+  int64_t device_budget_bytes;
+} pkv_pool_desc;
+
+/*
+ * A page selection (device memory), as written by pkv_select_topk_pages:
+ *   pages  int32 [n_qpages][Hkv][stride]: ascending absolute key-page ids of
+ *          each (query page, KV head), entries past count are ignored;
+ *   count  int32 [n_qpages][Hkv].
+ * Query page i of a chunk that starts at q_pos0 is absolute page
+ * q_pos0 / P + i.  Every list must contain the query page itself and
+ * page 0, ascend strictly, and hold only pages <= the query page.
+ */
+typedef struct {
+  const int32_t* pages;
+  const int32_t* count;
+  int32_t n_qpages;
+  int32_t stride;
+} pkv_sel;
+
+/* Create a pool (allocates every buffer up front; never reallocates, so the
+ * pool's footprint is exactly the page bytes -- de 2.B: no reallocation or
+ * fragmentation when pages are appended).  Page tables start as the
+ * identity (logical page j -> slot j), gradients start at zero.
+ * Synchronous.  *out receives the pool. */
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
+
+/* Destroy a pool: synchronises the device, then frees everything.  NULL is
+ * accepted and ignored. */
+pkv_status pkv_pool_destroy(pkv_pool* pool);
+
+/* Set the page table of (layer, kv_head) from host memory: host_slots[j] is
+ * the slot of logical page j, for j < n (n <= max_logical_pages; the rest of
+ * the table is left as is).  Entries must be distinct and in [0, n_slots).
+ * Must be called before any append to that layer.  Synchronous. */
+pkv_status pkv_page_table_set(pkv_pool* pool, int32_t layer, int32_t kv_head,
+                              const int32_t* host_slots, int32_t n);
+
+/* Number of tokens appended so far to `layer` (host value; -1 on bad args). */
+int64_t pkv_length(const pkv_pool* pool, int32_t layer);
+
+/* Append n_tok tokens at positions [pos0, pos0 + n_tok) to `layer`:
+ * k, v are device [n_tok][Hkv][d] in kv_dtype.  pos0 must equal the current
+ * length (no overwrite), and the pages must fit the table.  Token s goes to
+ * slot table[g][s / P], row s % P.  The representative vector of every page
+ * the call writes is recomputed as the fp32 mean of that page's keys present
+ * so far (nl "Methodologie": one representative vector per page). */
+pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, int64_t pos0, int64_t n_tok,
+                         const void* k, const void* v, hipStream_t stream);
+
+/* Forward attention of one query chunk over the paged cache of `layer`
+ * (de 2.B custom kernels; sciencestack Figure 3).
+ *   q_pos0  absolute position of the chunk's first query; q_pos0 % P == 0 and
+ *           q_pos0 + n_q <= pkv_length(layer) (the chunk's own K/V are
+ *           appended first).
+ *   scale   softmax scale (1/sqrt(d) for standard attention).
+ *   q       device [n_q][n_q_heads][d], kv_dtype.
+ *   sel     NULL for dense causal attention, else a selection covering the
+ *           chunk's query pages (sel->n_qpages == ceil(n_q / P)).
+ *   o       device [n_q][n_q_heads][d], kv_dtype (written).
+ *   lse     device [n_q_heads][n_q] fp32 (written), natural log.
+ * Accumulation is fp32 (bf16 inputs go through bf16 MFMA with fp32
+ * accumulate; fp32 inputs use fp32 arithmetic). */
+pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                        int32_t n_q_heads, float scale, const void* q, const pkv_sel* sel,
+                        void* o, float* lse, hipStream_t stream);
+
+/* Recompute-backward of one query chunk (de 2.A recomputation, 2.B in-place
+ * atomic gradient accumulation; sciencestack Figure 3).  Takes the forward's
+ * q, o and lse, the upstream gradient dout (device [n_q][n_q_heads][d],
+ * kv_dtype) and the same sel as the forward.  Writes dq (device
+ * [n_q][n_q_heads][d] fp32, overwritten) and ADDS dK, dV into the layer's
+ * gradient pool with fp32 atomics (dK/dV of a multi-chunk run are the sum
+ * of every chunk's contribution).  Uses a library-owned scratch buffer for
+ * D = rowsum(dO * O), grown with hipMalloc when a larger chunk arrives. */
+pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                        int32_t n_q_heads, float scale, const void* q, const void* o,
+                        const void* dout, const float* lse, const pkv_sel* sel, float* dq,
+                        hipStream_t stream);
+
+/* Page-level top-K selection for every query page of one chunk (de 2.D; nl
+ * "Methodologie"; sciencestack Figure 5).  For query page i (absolute) and
+ * KV head g:
+ *   qbar = fp32 mean of q over the page's tokens in the chunk and the G query
+ *          heads of group g;  kbar_j = the page's representative vector;
+ *   score_j = fp32 dot(qbar, kbar_j) for candidates
+ *          j in [n_sink, i - n_local] (the pages between the sinks and the
+ *          local window);
+ *   kept = the top_k candidates by score, ties to the lower page index;
+ *   written list = {0 .. n_sink-1} U {i-n_local+1 .. i} U kept, ascending,
+ *          clipped to [0, i].
+ * q is device [n_q][n_q_heads][d] in kv_dtype.  sel_pages is device
+ * [ceil(n_q/P)][Hkv][sel_stride] int32 with sel_stride >=
+ * top_k + n_sink + n_local (unused entries set to -1); sel_count is device
+ * [ceil(n_q/P)][Hkv] int32.  Uses library-owned scratch for the scores. */
+pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                                 int32_t n_q_heads, const void* q, int32_t top_k,
+                                 int32_t n_sink, int32_t n_local, int32_t* sel_pages,
+                                 int32_t* sel_count, int32_t sel_stride, hipStream_t stream);
+
+/* Host-tier pools only (PKV_OK and no work otherwise): bring the pages of
+ * `layer` that `sel` names (every query page, every KV head; sel == NULL:
+ * every appended page) from pinned host memory into the HBM window, on
+ * copy_stream, without a host synchronisation (de 2.C: prefetch of the next
+ * layer while the current one computes).  with_grads != 0 also brings the
+ * pages' dK/dV (host gradient dtype -> fp32).  The window slot the layer
+ * lands in is not overwritten before earlier attention calls that read it
+ * have finished (the library orders this with events).  `ready`, if not
+ * NULL, is recorded on copy_stream when the copies are done; attention calls
+ * on this layer wait for it on their own stream automatically. */
+pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
+                              int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready);
+
+/* Host-tier pools only: write the dK/dV pages of `layer` that the last
+ * prefetch with grads brought in back to host memory (fp32 -> host gradient
+ * dtype) on copy_stream, after the attention calls on `layer` issued so far
+ * have finished.  `done`, if not NULL, is recorded when the copies finish. */
+pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_stream,
+                               hipEvent_t done);
+
+/* Zero the dK/dV pool of `layer` (all slots; the host tier too in host-tier
+ * mode, synchronously). */
+pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
+
+/* Export (copy, never alias) pool contents of `layer` in logical order, for
+ * tests and tooling:
+ *   PKV_K, PKV_V   -> dst device [n_tok][Hkv][d] kv_dtype;
+ *   PKV_DK, PKV_DV -> dst device [n_tok][Hkv][d] fp32;
+ *   PKV_REPS       -> dst device [n_pages][Hkv][d] fp32;
+ * where n_tok = pkv_length(layer) and n_pages = ceil(n_tok / P).  In
+ * host-tier mode K/V/dK/dV are read from the host tier (synchronises the
+ * device first). */
+pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst,
+                          hipStream_t stream);
+
+/* Bytes the pool holds on the device and in pinned host memory. */
+pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* host_bytes);
+
+/* Thread-local message of the last non-OK status returned on this thread. */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

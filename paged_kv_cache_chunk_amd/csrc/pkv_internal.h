@@ -1,0 +1,90 @@
+// Internal declarations shared by the host side of libpkv and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Device view of one layer's pools.
+//   k, v    [Hkv][slots][P][d] in the pool's kv dtype
+//   dk, dv  [Hkv][slots][P][d] fp32 (accumulated in place with atomics)
+//   reps    [Hkv][slots][d] fp32 page representative (mean of the page's keys)
+//   table   [Hkv][max_logical] int32 logical page -> slot
+struct LayerDev {
+  void* k;
+  void* v;
+  float* dk;
+  float* dv;
+  float* reps;
+  const int32_t* table;
+};
+
+struct Geom {
+  int hkv;
+  int d;
+  int page;
+  int slots;
+  int max_logical;
+};
+
+// Selection in device memory; pages == nullptr means dense.
+struct SelDev {
+  const int32_t* pages;
+  const int32_t* count;
+  int n_qpages;
+  int stride;
+};
+
+// Everything an attention launch needs.
+struct AttnCall {
+  LayerDev L;
+  Geom g;
+  int hq;
+  int64_t q_pos0;
+  int n_q;
+  float scale;
+  SelDev sel;
+  const void* q;
+  const void* o;
+  const void* dout;
+  void* o_out;
+  float* lse;
+  const float* lse_in;
+  float* delta;  // D = rowsum(dO * O), [hq][n_q]
+  float* dq;
+};
+
+// ---- kernels in kv_pages.hip
+hipError_t launch_append(const LayerDev& L, const Geom& g, int elem_bytes, int64_t pos0,
+                         int64_t n_tok, const void* k, const void* v, hipStream_t s);
+hipError_t launch_reps(const LayerDev& L, const Geom& g, bool bf16, int64_t first_page,
+                       int64_t n_pages, int64_t length, hipStream_t s);
+hipError_t launch_export(const LayerDev& L, const Geom& g, int what, int elem_bytes,
+                         int64_t n_tok, void* dst, hipStream_t s);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+// ---- kernels in select_topk.hip
+hipError_t launch_select(const LayerDev& L, const Geom& g, bool bf16, int hq, int64_t q_pos0,
+                         int n_q, const void* q, int top_k, int n_sink, int n_local,
+                         int32_t* sel_pages, int32_t* sel_count, int sel_stride,
+                         float* scratch, hipStream_t s);
+int64_t select_scratch_floats(const Geom& g, int64_t q_pos0, int n_q, int n_sink, int n_local);
+
+// ---- kernels in attn_f32.hip
+hipError_t launch_fwd_f32(const AttnCall& c, hipStream_t s);
+hipError_t launch_bwd_f32(const AttnCall& c, hipStream_t s);
+
+// ---- kernels in attn_bf16.hip
+hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s);
+hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s);
+
+// ---- kernels in attn_common.hip
+hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s);
+
+// ---- host tier (offload.hip)
+hipError_t launch_gather_host_pages(const void* host_base, void* dev_base,
+                                    const int32_t* page_list, const int32_t* n_list,
+                                    int64_t page_bytes, int64_t max_pages, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,267 @@
+// Pool allocation, appends, exports and the host tier (pinned host pools with
+// a two-layer HBM window filled on a side stream).
+//
+// "Out of the Memory Barrier" (gist.science de, section 2.B: fixed-size
+// pages, no reallocation on append; section 2.C and gist.science nl,
+// "Methodologie": the KV cache and its gradients move asynchronously between
+// pinned host memory and the GPU on separate streams, the next layer being
+// fetched while the current one computes).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "pkv_pool.h"
+
+namespace pkv {
+namespace {
+
+pkv_status dev_alloc(pkv_pool* p, void** ptr, int64_t bytes, const char* what) {
+  *ptr = nullptr;
+  if (bytes <= 0) return PKV_OK;
+  hipError_t e = hipMalloc(ptr, (size_t)bytes);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    (void)hipGetLastError();
+    return pool_fail(PKV_ENOMEM, what);
+  }
+  p->device_bytes += bytes;
+  e = hipMemset(*ptr, 0, (size_t)bytes);
+  if (e != hipSuccess) return pool_hip_fail(e, "hipMemset (pool init)");
+  return PKV_OK;
+}
+
+pkv_status host_alloc(pkv_pool* p, void** hptr, void** dptr, int64_t bytes) {
+  *hptr = *dptr = nullptr;
+  hipError_t e = hipHostMalloc(hptr, (size_t)bytes, hipHostMallocMapped);
+  if (e != hipSuccess) {
+    *hptr = nullptr;
+    (void)hipGetLastError();
+    return pool_fail(PKV_ENOMEM, "pinned host allocation for the host tier failed");
+  }
+  p->host_bytes += bytes;
+  e = hipHostGetDevicePointer(dptr, *hptr, 0);
+  if (e != hipSuccess) return pool_hip_fail(e, "hipHostGetDevicePointer");
+  return PKV_OK;
+}
+
+int grad_host_bytes(const pkv_pool* p) { return p->desc.host_grad_dtype == PKV_BF16 ? 2 : 4; }
+
+}  // namespace
+
+pkv_status pool_allocate(pkv_pool* p) {
+  const pkv_pool_desc& d = p->desc;
+  const int copies = d.host_tier ? pkv_pool::kWindow : d.n_layers;
+  pkv_status st;
+  const int64_t kvb = p->layer_elems * p->kv_bytes * copies;
+  const int64_t grb = p->layer_elems * 4 * copies;
+  const int64_t repb = (int64_t)d.n_layers * d.n_kv_heads * d.n_slots * d.head_dim * 4;
+  const int64_t tabb = (int64_t)d.n_layers * d.n_kv_heads * d.max_logical_pages * 4;
+  const int64_t needb = d.host_tier ? (int64_t)pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
+  if (d.host_tier && d.device_budget_bytes > 0 &&
+      2 * kvb + 2 * grb + repb + tabb + needb > d.device_budget_bytes)
+    return pool_fail(PKV_ENOMEM, "host-tier window does not fit device_budget_bytes");
+  if ((st = dev_alloc(p, &p->d_k, kvb, "device allocation of the K pool failed")) != PKV_OK) return st;
+  if ((st = dev_alloc(p, &p->d_v, kvb, "device allocation of the V pool failed")) != PKV_OK) return st;
+  if ((st = dev_alloc(p, (void**)&p->d_dk, grb, "device allocation of the dK pool failed")) != PKV_OK) return st;
+  if ((st = dev_alloc(p, (void**)&p->d_dv, grb, "device allocation of the dV pool failed")) != PKV_OK) return st;
+  if ((st = dev_alloc(p, (void**)&p->d_reps, repb, "device allocation of the representatives failed")) != PKV_OK) return st;
+  if ((st = dev_alloc(p, (void**)&p->d_table, tabb, "device allocation of the page tables failed")) != PKV_OK) return st;
+  hipError_t e = hipMemcpy(p->d_table, p->h_table.data(), (size_t)tabb, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return pool_hip_fail(e, "hipMemcpy (page tables)");
+  if (d.host_tier) {
+    if ((st = dev_alloc(p, (void**)&p->d_need, needb, "device allocation of the window map failed")) != PKV_OK) return st;
+    for (int w = 0; w < pkv_pool::kWindow; ++w) {
+      if ((e = hipEventCreateWithFlags(&p->ev_compute[w], hipEventDisableTiming)) != hipSuccess)
+        return pool_hip_fail(e, "hipEventCreate");
+      if ((e = hipEventCreateWithFlags(&p->ev_ready[w], hipEventDisableTiming)) != hipSuccess)
+        return pool_hip_fail(e, "hipEventCreate");
+      if ((e = hipEventCreateWithFlags(&p->ev_wb[w], hipEventDisableTiming)) != hipSuccess)
+        return pool_hip_fail(e, "hipEventCreate");
+    }
+    const int64_t hkv = p->layer_elems * p->kv_bytes;
+    const int64_t hgr = p->layer_elems * grad_host_bytes(p);
+    p->h_k.assign(d.n_layers, nullptr);
+    p->h_v.assign(d.n_layers, nullptr);
+    p->h_dk.assign(d.n_layers, nullptr);
+    p->h_dv.assign(d.n_layers, nullptr);
+    p->m_k.assign(d.n_layers, nullptr);
+    p->m_v.assign(d.n_layers, nullptr);
+    p->m_dk.assign(d.n_layers, nullptr);
+    p->m_dv.assign(d.n_layers, nullptr);
+    for (int l = 0; l < d.n_layers; ++l) {
+      if ((st = host_alloc(p, &p->h_k[l], &p->m_k[l], hkv)) != PKV_OK) return st;
+      if ((st = host_alloc(p, &p->h_v[l], &p->m_v[l], hkv)) != PKV_OK) return st;
+      if ((st = host_alloc(p, &p->h_dk[l], &p->m_dk[l], hgr)) != PKV_OK) return st;
+      if ((st = host_alloc(p, &p->h_dv[l], &p->m_dv[l], hgr)) != PKV_OK) return st;
+      // zero on the device through the mapping (fast, and never leaves NaN bit
+      // patterns in rows that a tile reads past the appended length)
+      if ((e = launch_fill_zero(p->m_k[l], hkv, nullptr)) != hipSuccess ||
+          (e = launch_fill_zero(p->m_v[l], hkv, nullptr)) != hipSuccess ||
+          (e = launch_fill_zero(p->m_dk[l], hgr, nullptr)) != hipSuccess ||
+          (e = launch_fill_zero(p->m_dv[l], hgr, nullptr)) != hipSuccess)
+        return pool_hip_fail(e, "host tier zero fill");
+    }
+  }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return pool_hip_fail(e, "hipDeviceSynchronize (pool init)");
+  return PKV_OK;
+}
+
+pkv_status pool_release(pkv_pool* p) {
+  pkv_status st = PKV_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) st = pool_hip_fail(e, "hipDeviceSynchronize (pool destroy)");
+  void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_delta,
+                 p->d_select, p->d_need};
+  for (void* x : dev)
+    if (x) (void)hipFree(x);
+  for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
+    for (void* x : *v)
+      if (x) (void)hipHostFree(x);
+  for (int w = 0; w < pkv_pool::kWindow; ++w) {
+    if (p->ev_compute[w]) (void)hipEventDestroy(p->ev_compute[w]);
+    if (p->ev_ready[w]) (void)hipEventDestroy(p->ev_ready[w]);
+    if (p->ev_wb[w]) (void)hipEventDestroy(p->ev_wb[w]);
+  }
+  return st;
+}
+
+// The K/V/dK/dV bases a kernel should read or write for `layer`: the HBM
+// pool, or the device-visible mapping of the host tier.
+static LayerDev store_view(pkv_pool* p, int layer) {
+  LayerDev L = layer_view(p, layer);
+  if (p->desc.host_tier) {
+    L.k = p->m_k[layer];
+    L.v = p->m_v[layer];
+    L.dk = (float*)p->m_dk[layer];
+    L.dv = (float*)p->m_dv[layer];
+  }
+  return L;
+}
+
+pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, const void* k,
+                       const void* v, hipStream_t s) {
+  const LayerDev L = store_view(p, layer);
+  const Geom g = geom(p);
+  hipError_t e = launch_append(L, g, p->kv_bytes, pos0, n_tok, k, v, s);
+  if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: append launch");
+  const int64_t first = pos0 / g.page;
+  const int64_t last = (pos0 + n_tok - 1) / g.page;
+  e = launch_reps(L, g, p->desc.kv_dtype == PKV_BF16, first, last - first + 1, pos0 + n_tok, s);
+  if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: representative launch");
+  return PKV_OK;
+}
+
+pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s) {
+  hipError_t e;
+  if (!p->desc.host_tier) {
+    const LayerDev L = layer_view(p, layer);
+    if ((e = launch_fill_zero(L.dk, p->layer_elems * 4, s)) != hipSuccess ||
+        (e = launch_fill_zero(L.dv, p->layer_elems * 4, s)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_grad_zero");
+    return PKV_OK;
+  }
+  const int64_t hgr = p->layer_elems * grad_host_bytes(p);
+  if ((e = launch_fill_zero(p->m_dk[layer], hgr, s)) != hipSuccess ||
+      (e = launch_fill_zero(p->m_dv[layer], hgr, s)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_grad_zero (host tier)");
+  const int w = p->window_of(layer);
+  if (p->window_layer[w] == layer) {
+    const LayerDev L = layer_view(p, layer);
+    if ((e = launch_fill_zero(L.dk, p->layer_elems * 4, s)) != hipSuccess ||
+        (e = launch_fill_zero(L.dv, p->layer_elems * 4, s)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_grad_zero (window)");
+  }
+  if ((e = hipStreamSynchronize(s)) != hipSuccess) return pool_hip_fail(e, "pkv_grad_zero: sync");
+  return PKV_OK;
+}
+
+pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s) {
+  const Geom g = geom(p);
+  const int64_t n_tok = p->length[layer];
+  hipError_t e;
+  if (!p->desc.host_tier || what == PKV_REPS) {
+    e = launch_export(layer_view(p, layer), g, what, p->kv_bytes, n_tok, dst, s);
+  } else {
+    if ((e = hipDeviceSynchronize()) != hipSuccess) return pool_hip_fail(e, "pkv_read_pages: sync");
+    if ((what == PKV_DK || what == PKV_DV) && p->desc.host_grad_dtype == PKV_BF16)
+      e = launch_host_export(p, layer, what, n_tok, dst, s);
+    else
+      e = launch_export(store_view(p, layer), g, what, p->kv_bytes, n_tok, dst, s);
+  }
+  if (e != hipSuccess) return pool_hip_fail(e, "pkv_read_pages: launch");
+  return PKV_OK;
+}
+
+pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s) {
+  if (!p->desc.host_tier) return PKV_OK;
+  const int w = p->window_of(layer);
+  if (p->window_layer[w] != layer)
+    return pool_fail(PKV_ESTATE, "layer is not in the HBM window: call pkv_prefetch_pages first");
+  if (p->ready_recorded[w]) {
+    hipError_t e = hipStreamWaitEvent(s, p->ev_ready[w], 0);
+    if (e != hipSuccess) return pool_hip_fail(e, "hipStreamWaitEvent (window ready)");
+  }
+  return PKV_OK;
+}
+
+pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s) {
+  if (!p->desc.host_tier) return PKV_OK;
+  const int w = p->window_of(layer);
+  hipError_t e = hipEventRecord(p->ev_compute[w], s);
+  if (e != hipSuccess) return pool_hip_fail(e, "hipEventRecord (window compute)");
+  p->compute_recorded[w] = true;
+  return PKV_OK;
+}
+
+pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_grads,
+                         hipStream_t cs, hipEvent_t ready) {
+  const int w = p->window_of(layer);
+  const pkv_pool_desc& d = p->desc;
+  hipError_t e;
+  if (p->compute_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (window reuse)");
+  }
+  if (p->wb_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
+  }
+  uint8_t* need = p->d_need + (int64_t)w * d.n_kv_heads * d.max_logical_pages;
+  const int64_t n_pages = (p->length[layer] + d.page_size - 1) / d.page_size;
+  if ((e = launch_need_clear(need, (int64_t)d.n_kv_heads * d.max_logical_pages, cs)) != hipSuccess ||
+      (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_prefetch_pages: page map");
+  p->window_layer[w] = layer;
+  p->window_grads[w] = with_grads;
+  if ((e = launch_fetch_pages(p, layer, w, with_grads, cs)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
+  if ((e = hipEventRecord(p->ev_ready[w], cs)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventRecord (window ready)");
+  p->ready_recorded[w] = true;
+  if (ready && (e = hipEventRecord(ready, cs)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventRecord (caller ready)");
+  return PKV_OK;
+}
+
+pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t done) {
+  const int w = p->window_of(layer);
+  if (p->window_layer[w] != layer || !p->window_grads[w])
+    return pool_fail(PKV_ESTATE,
+                     "pkv_writeback_grads: the layer's gradients were not prefetched into the window");
+  hipError_t e;
+  if (p->compute_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (writeback)");
+  }
+  if ((e = launch_writeback_pages(p, layer, w, cs)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_writeback_grads: launch");
+  if ((e = hipEventRecord(p->ev_wb[w], cs)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventRecord (writeback)");
+  p->wb_recorded[w] = true;
+  if (done && (e = hipEventRecord(done, cs)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventRecord (writeback done)");
+  return PKV_OK;
+}
+
+}  // namespace pkv

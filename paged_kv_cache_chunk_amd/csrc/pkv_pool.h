@@ -1,0 +1,82 @@
+// The pool object behind the opaque pkv_pool handle, and the pool-level
+// operations the C ABI dispatches to (pkv_pool.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+struct pkv_pool {
+  pkv_pool_desc desc{};
+  int kv_bytes = 2;          // bytes per K/V element
+  int64_t layer_elems = 0;   // Hkv * slots * P * d
+  std::vector<int64_t> length;    // appended tokens per layer
+  std::vector<int32_t> h_table;   // [layers][Hkv][max_logical], host mirror
+
+  // Device buffers.  Without a host tier: n_layers copies of K, V, dK, dV.
+  // With a host tier: kWindow copies (the HBM window).
+  void* d_k = nullptr;
+  void* d_v = nullptr;
+  float* d_dk = nullptr;
+  float* d_dv = nullptr;
+  float* d_reps = nullptr;        // [layers][Hkv][slots][d]
+  int32_t* d_table = nullptr;     // [layers][Hkv][max_logical]
+  void* d_delta = nullptr;        // attn_bwd scratch
+  int64_t delta_bytes = 0;
+  void* d_select = nullptr;       // select scratch
+  int64_t select_bytes = 0;
+  int64_t device_bytes = 0;
+  int64_t host_bytes = 0;
+
+  // Host tier (pinned, device-mapped), per layer.
+  static constexpr int kWindow = 2;
+  std::vector<void*> h_k, h_v, h_dk, h_dv;      // host pointers
+  std::vector<void*> m_k, m_v, m_dk, m_dv;      // device-visible aliases
+  int window_layer[kWindow] = {-1, -1};
+  bool window_grads[kWindow] = {false, false};  // grads of the needed pages were fetched
+  hipEvent_t ev_compute[kWindow] = {nullptr, nullptr};  // after the last attention call
+  hipEvent_t ev_ready[kWindow] = {nullptr, nullptr};    // after the last prefetch
+  hipEvent_t ev_wb[kWindow] = {nullptr, nullptr};       // after the last grad writeback
+  bool wb_recorded[kWindow] = {false, false};
+  bool compute_recorded[kWindow] = {false, false};
+  bool ready_recorded[kWindow] = {false, false};
+  uint8_t* d_need = nullptr;      // [kWindow][Hkv][max_logical] pages held by the window
+
+  int window_of(int layer) const { return layer % kWindow; }
+};
+
+namespace pkv {
+
+pkv_status pool_fail(pkv_status st, const char* msg);
+pkv_status pool_hip_fail(hipError_t e, const char* what);
+LayerDev layer_view(pkv_pool* p, int layer);
+Geom geom(const pkv_pool* p);
+pkv_status ensure_scratch(void** buf, int64_t* have, int64_t need);
+
+pkv_status pool_allocate(pkv_pool* p);
+pkv_status pool_release(pkv_pool* p);
+pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, const void* k,
+                       const void* v, hipStream_t s);
+pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s);
+pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s);
+pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s);
+pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s);
+pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_grads,
+                         hipStream_t copy_stream, hipEvent_t ready);
+pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t copy_stream, hipEvent_t done);
+
+// offload.hip
+hipError_t launch_need_clear(uint8_t* need, int64_t n, hipStream_t s);
+hipError_t launch_need_mark(uint8_t* need, const pkv_sel* sel, int hkv, int max_logical,
+                            int64_t n_pages_all, hipStream_t s);
+hipError_t launch_fetch_pages(const pkv_pool* p, int layer, int window, bool with_grads,
+                              hipStream_t s);
+hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipStream_t s);
+hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,
+                              hipStream_t s);
+
+}  // namespace pkv
