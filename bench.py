@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV chunk attention hot path on one MI355X.
+
+One step = one attention layer over the whole context, chunk by chunk, as a
+chunk-recurrent training step runs it: the layer's pool is reset and every
+chunk's K/V appended (forward sweep), then, in reverse chunk order (backward
+sweep), each chunk runs (page selection in top-K mode) + attention forward +
+recompute-backward, the backward adding dK/dV into the paged gradient pool.
+Inputs (seeded, synthetic, Qwen2.5-7B attention shape) are resident in HBM
+before the timed region.
+
+Headline: 128K-token dense context (chunks of 12288, pages of 128); the
+256K-token page top-K context (top-K 64 + page 0 + 2 local pages, chunks of
+4096) is reported in the same line.  FLOPs use the algorithmic count
+14 * d * Hq per attended (query, key) pair (4 d forward + 10 d backward).
+
+Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dq": 6, "dkdv": 8}  # x d x Hq per attended pair
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "paged_kv_cache_chunk_amd", "csrc", "attn_bf16.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def sparse_pairs(sel_counts, chunk_rows, page: int, G: int) -> int:
+    """Attended (query, key) pairs x heads from the selection counts of one chunk.
+    Every listed page before the query page is complete; the query page itself
+    contributes its causal triangle."""
+    total = 0
+    nqp, hkv = sel_counts.shape
+    for i in range(nqp):
+        rows = min(page, chunk_rows - i * page)
+        for g in range(hkv):
+            c = int(sel_counts[i, g])
+            total += G * ((c - 1) * page * rows + rows * (rows + 1) // 2)
+    return total
+
+
+class LayerBench:
+    """Inputs, pool and buffers of one single-layer workload."""
+
+    def __init__(self, cfg, seed: int = 0):
+        import torch
+        import paged_kv_cache_chunk_amd as pkv
+        from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, Sparse
+        from synthetic.gpu import GpuWorkload
+
+        self.cfg = cfg
+        self.pkv = pkv
+        self.w = GpuWorkload(cfg, seed=seed)
+        t0 = time.time()
+        self.chunks = [self.w.chunk(c) for c in range(cfg.n_chunks)]
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name}: inputs generated on the GPU in {time.time() - t0:.1f}s")
+        kvd = pkv.PKV_BF16 if cfg.dtype == "bf16" else pkv.PKV_F32
+        self.pool = pkv.pkv_pool_create(1, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, kvd)
+        tab = self.w.table()
+        for g in range(cfg.hkv):
+            pkv.pkv_page_table_set(self.pool, 0, g, tab[g])
+        self.sparse = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local) if cfg.sparse else None
+        dt = self.w.dtype
+        self.bufs = {}
+        for ch in self.chunks:
+            n = ch["q"].shape[0]
+            if n not in self.bufs:
+                self.bufs[n] = ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page, dt, self.sparse)
+        self.sel_counts = {}
+
+    def step(self, keep_counts: bool = False):
+        pkv, cfg = self.pkv, self.cfg
+        pkv.pkv_pool_reset(self.pool, 0)
+        pkv.pkv_grad_zero(self.pool, 0)
+        for ch in self.chunks:
+            pkv.pkv_append_kv(self.pool, 0, ch["q_pos0"], ch["k"], ch["v"])
+        for c in reversed(range(len(self.chunks))):
+            ch = self.chunks[c]
+            b = self.bufs[ch["q"].shape[0]]
+            if self.sparse is not None:
+                pkv.pkv_select_topk_pages(self.pool, 0, ch["q_pos0"], ch["q"], self.sparse.top_k,
+                                          b.sel[0], b.sel[1], self.sparse.n_sink,
+                                          self.sparse.n_local)
+                if keep_counts:
+                    self.sel_counts[c] = b.sel[1].cpu().numpy()
+            pkv.pkv_attn_fwd(self.pool, 0, ch["q_pos0"], ch["q"], b.o, b.lse, cfg.scale, sel=b.sel)
+            pkv.pkv_attn_bwd(self.pool, 0, ch["q_pos0"], ch["q"], b.o, ch["do"], b.lse, b.dq,
+                             cfg.scale, sel=b.sel)
+
+    def pairs(self) -> int:
+        """Attended (query, key) pairs summed over query heads, one step."""
+        cfg = self.cfg
+        if self.sparse is None:
+            N = cfg.n_ctx
+            return cfg.hq * N * (N + 1) // 2
+        return sum(sparse_pairs(self.sel_counts[c], self.chunks[c]["q"].shape[0], cfg.page,
+                                cfg.group) for c in range(len(self.chunks)))
+
+    def run(self, steps: int, warmup: int):
+        import torch
+        pkv = self.pkv
+        for i in range(warmup):
+            self.step(keep_counts=(i == 0))
+        if warmup == 0:
+            self.step(keep_counts=True)
+        torch.cuda.synchronize()
+        pkv.pkv_kernel_timing(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        ktimes = pkv.pkv_kernel_times()
+        pkv.pkv_kernel_timing(False)
+        return ms, ktimes
+
+
+def kernel_table(lb: LayerBench, ms_step: float, ktimes: dict, steps: int) -> dict:
+    cfg = lb.cfg
+    pairs = lb.pairs()
+    out = {}
+    for k, (tot, n) in ktimes.items():
+        if n == 0:
+            continue
+        e = {"launches_per_step": n // steps, "avg_ms": tot / n, "ms_per_step": tot / steps}
+        if k in KERNEL_FLOPS_PER_PAIR:
+            fl = KERNEL_FLOPS_PER_PAIR[k] * cfg.d * pairs  # pairs already x Hq
+            e["tflops"] = fl * steps / (tot * 1e-3) / 1e12
+        out[k] = e
+    return out
+
+
+def cpu_baseline(lb: LayerBench, rows: int) -> dict:
+    """The fp64 oracle on a bounded sample of the workload: the last `rows`
+    query rows of the context (all heads), forward + backward against every
+    key, timed on this host; scaled to tokens/s of the whole workload by the
+    share of attended pairs the sample covers."""
+    import numpy as np
+    import torch
+    import oracle
+
+    cfg = lb.cfg
+    N = cfg.n_ctx
+    ks, vs = [], []
+    for ch in lb.chunks:
+        ks.append(ch["k"].float().cpu().numpy())
+        vs.append(ch["v"].float().cpu().numpy())
+    k = np.concatenate(ks)
+    v = np.concatenate(vs)
+    last = lb.chunks[-1]
+    q = last["q"][-rows:].float().cpu().numpy()
+    do = last["do"][-rows:].float().cpu().numpy()
+    q_pos0 = N - rows
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    oracle.attn_bwd(q, k, v, do, q_pos0, cfg.scale, cfg.page)
+    dt = time.perf_counter() - t0
+    sample_pairs = rows * q_pos0 + rows * (rows + 1) // 2
+    total_pairs = N * (N + 1) // 2
+    return {"value": N * (sample_pairs / total_pairs) / dt, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd of the last {rows} query rows x {cfg.hq} heads "
+                      f"against all {N} keys ({sample_pairs} pairs/head of {total_pairs}); "
+                      f"{dt:.1f}s, scaled by the pair share"}
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    e = data.get(f"{workload}:{kernel}")
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="qwen_128k_dense")
+    ap.add_argument("--sparse-workload", default="qwen_256k_topk",
+                    help="second workload in the same line ('none' to skip)")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="query rows in the oracle's CPU sample (0 skips it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synthetic import get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    cfg = get_config(args.workload)
+    lb = LayerBench(cfg)
+    log(f"[bench] {cfg.name}: warmup {args.warmup}, timing {args.steps} steps")
+    ms, kt = lb.run(args.steps, args.warmup)
+    pairs = lb.pairs()
+    flops = 14 * cfg.d * pairs
+    ktab = kernel_table(lb, ms, kt, args.steps)
+    log(f"[bench] {cfg.name}: {ms:.1f} ms/step, {flops / ms / 1e9:.1f} TFLOP/s; kernels {ktab}")
+
+    dom = max((k for k in ktab if k in KERNEL_FLOPS_PER_PAIR), key=lambda k: ktab[k]["ms_per_step"])
+    achieved = ktab[dom]["tflops"]
+    roofline = {"bound": "mfma", "kernel": f"{dom}_bf16_kernel", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dom, cfg.name),
+                "flops_per_pair": f"{KERNEL_FLOPS_PER_PAIR[dom]}*d*Hq"}
+
+    line = {
+        "metric": "attn fwd+bwd tokens/s per layer, 128K dense & 256K top-K; % bf16 MFMA peak",
+        "value": round(cfg.n_ctx / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: 1 attention layer, Hq {cfg.hq}, Hkv {cfg.hkv}, "
+                               f"d {cfg.d}, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, "
+                               f"pages of {cfg.page}, dense causal",
+                   "context": cfg.n_ctx, "chunk": cfg.chunk, "page": cfg.page},
+        "tflops": round(flops / ms / 1e9, 1),
+        "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
+                    for k, e in ktab.items()},
+        "roofline": roofline,
+    }
+
+    if args.sparse_workload and args.sparse_workload != "none":
+        scfg = get_config(args.sparse_workload)
+        del lb
+        torch.cuda.empty_cache()
+        sb = LayerBench(scfg)
+        log(f"[bench] {scfg.name}: warmup {args.warmup}, timing {args.steps} steps")
+        sms, skt = sb.run(args.steps, args.warmup)
+        spairs = sb.pairs()
+        sfl = 14 * scfg.d * spairs
+        sktab = kernel_table(sb, sms, skt, args.steps)
+        log(f"[bench] {scfg.name}: {sms:.1f} ms/step, {sfl / sms / 1e9:.1f} TFLOP/s; {sktab}")
+        line["topk_256k"] = {
+            "workload": f"{scfg.name}: {scfg.n_ctx} tokens, chunks of {scfg.chunk}, top-K "
+                        f"{scfg.top_k} + {scfg.n_sink} sink + {scfg.n_local} local pages",
+            "tokens_per_s": round(scfg.n_ctx / (sms * 1e-3), 1),
+            "ms_per_step": round(sms, 3),
+            "tflops": round(sfl / sms / 1e9, 1),
+            "mfma_frac": round(sfl / sms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "attended_pairs_x_heads": spairs,
+            "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                            for kk, vv in e.items()} for k, e in sktab.items()},
+        }
+        lb = LayerBench(cfg) if args.cpu_rows else None
+
+    if args.cpu_rows:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        line["cpu_baseline"] = cpu_baseline(lb, args.cpu_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

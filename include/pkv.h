@@ -242,6 +242,33 @@ pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
 pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst,
                           hipStream_t stream);
 
+/* Forget the tokens of `layer` (length back to 0) so that a new sequence can
+ * be appended; no memory is freed or cleared (gradients are left as they
+ * are: pkv_grad_zero clears them).  Host-only, immediate. */
+pkv_status pkv_pool_reset(pkv_pool* pool, int32_t layer);
+
+/* Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by two HIP events recorded on the stream it is launched on, and
+ * its duration is added to the counter of its kind.  Kinds: */
+typedef enum {
+  PKV_KT_APPEND = 0,    /* append_kv scatter + page representatives */
+  PKV_KT_SELECT = 1,    /* select_topk_pages (query means, scores, top-K) */
+  PKV_KT_FWD = 2,       /* attention forward */
+  PKV_KT_DELTA = 3,     /* backward: D = rowsum(dO * O) */
+  PKV_KT_DQ = 4,        /* backward: dQ */
+  PKV_KT_DKDV = 5,      /* backward: dK/dV with atomics into the pool */
+  PKV_KT_FETCH = 6,     /* host tier: page fetch into the HBM window */
+  PKV_KT_WRITEBACK = 7, /* host tier: gradient writeback */
+  PKV_KT_COUNT = 8
+} pkv_kernel_kind;
+
+/* enable != 0: clear the counters and start timing; 0: stop timing. */
+pkv_status pkv_kernel_timing(int32_t enable);
+
+/* Wait for the recorded events, then write per-kind totals: total_ms[k] and
+ * launches[k] for k < n (n <= PKV_KT_COUNT).  Either array may be NULL. */
+pkv_status pkv_kernel_times(int32_t n, double* total_ms, int64_t* launches);
+
 /* Bytes the pool holds on the device and in pinned host memory. */
 pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* host_bytes);
 

@@ -25,8 +25,10 @@ EXPORTS = (
     "pkv_pool_create", "pkv_pool_destroy", "pkv_page_table_set", "pkv_length",
     "pkv_append_kv", "pkv_attn_fwd", "pkv_attn_bwd", "pkv_select_topk_pages",
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
-    "pkv_pool_bytes", "pkv_last_error",
+    "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
+    "pkv_kernel_times",
 )
+KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
 
 class PkvError(RuntimeError):
@@ -78,6 +80,9 @@ def lib() -> ctypes.CDLL:
             "pkv_grad_zero": [P, I32, VP],
             "pkv_read_pages": [P, I32, I32, VP, VP],
             "pkv_pool_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+            "pkv_pool_reset": [P, I32],
+            "pkv_kernel_timing": [I32],
+            "pkv_kernel_times": [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -226,6 +231,23 @@ def pkv_pool_bytes(pool: Pool) -> tuple[int, int]:
     a, b = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().pkv_pool_bytes(pool.handle, ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def pkv_pool_reset(pool: Pool, layer: int) -> None:
+    _check(lib().pkv_pool_reset(pool.handle, layer))
+
+
+def pkv_kernel_timing(enable: bool) -> None:
+    _check(lib().pkv_kernel_timing(int(enable)))
+
+
+def pkv_kernel_times() -> dict:
+    """{kind: (total_ms, launches)} since timing was enabled."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check(lib().pkv_kernel_times(n, ms, cnt))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def pkv_last_error() -> str:

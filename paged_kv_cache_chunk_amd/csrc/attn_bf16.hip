@@ -624,6 +624,7 @@ __global__ void __launch_bounds__(256, 1) dkdv_bf16_kernel(AttnCall c, int split
 
 hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s) {
   const int nqb = (c.n_q + BM - 1) / BM;
+  KernelTimer t(KT_FWD, s);
   hipLaunchKernelGGL(fwd_bf16_kernel, dim3(nqb, c.hq), dim3(256), 0, s, c, nqb);
   return hipGetLastError();
 }
@@ -632,14 +633,18 @@ hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
   hipError_t e = launch_delta(c, true, s);
   if (e != hipSuccess) return e;
   const int nqb = (c.n_q + BM - 1) / BM;
-  hipLaunchKernelGGL(dq_bf16_kernel, dim3(nqb, c.hq), dim3(256), 0, s, c, nqb);
-  e = hipGetLastError();
+  {
+    KernelTimer t(KT_DQ, s);
+    hipLaunchKernelGGL(dq_bf16_kernel, dim3(nqb, c.hq), dim3(256), 0, s, c, nqb);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const int64_t n_keys = c.q_pos0 + c.n_q;
   const int n_slabs = (int)((n_keys + 127) / 128);
   int splits = (2048 + n_slabs * c.g.hkv - 1) / (n_slabs * c.g.hkv);
   if (splits < 1) splits = 1;
   if (splits > 16) splits = 16;
+  KernelTimer t(KT_DKDV, s);
   hipLaunchKernelGGL(dkdv_bf16_kernel, dim3(n_slabs, c.g.hkv, splits), dim3(256), 0, s, c,
                      splits);
   return hipGetLastError();

@@ -43,6 +43,7 @@ __global__ void __launch_bounds__(256) delta_kernel(const void* __restrict__ o,
 
 hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s) {
   const int64_t n_rows = (int64_t)c.n_q * c.hq;
+  KernelTimer t(KT_DELTA, s);
   hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
                      c.o, c.dout, c.delta, c.hq, c.n_q, c.g.d, bf16);
   return hipGetLastError();

@@ -322,6 +322,7 @@ __global__ void __launch_bounds__(64) dkdv_f32_kernel(AttnCall c) {
 
 hipError_t launch_fwd_f32(const AttnCall& c, hipStream_t s) {
   const dim3 grid((c.n_q + kRows - 1) / kRows, c.hq);
+  KernelTimer t(KT_FWD, s);
   if (c.g.d == 64)
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, c);
   else
@@ -335,12 +336,19 @@ hipError_t launch_bwd_f32(const AttnCall& c, hipStream_t s) {
   const dim3 gq((c.n_q + kRows - 1) / kRows, c.hq);
   const int64_t n_keys = c.q_pos0 + c.n_q;
   const dim3 gk((unsigned)((n_keys + kRows - 1) / kRows), c.g.hkv);
-  if (c.g.d == 64) {
-    hipLaunchKernelGGL(dq_f32_kernel<64>, gq, dim3(64), 0, s, c);
-    hipLaunchKernelGGL(dkdv_f32_kernel<64>, gk, dim3(64), 0, s, c);
-  } else {
-    hipLaunchKernelGGL(dq_f32_kernel<128>, gq, dim3(64), 0, s, c);
-    hipLaunchKernelGGL(dkdv_f32_kernel<128>, gk, dim3(64), 0, s, c);
+  {
+    KernelTimer t(KT_DQ, s);
+    if (c.g.d == 64)
+      hipLaunchKernelGGL(dq_f32_kernel<64>, gq, dim3(64), 0, s, c);
+    else
+      hipLaunchKernelGGL(dq_f32_kernel<128>, gq, dim3(64), 0, s, c);
+  }
+  {
+    KernelTimer t(KT_DKDV, s);
+    if (c.g.d == 64)
+      hipLaunchKernelGGL(dkdv_f32_kernel<64>, gk, dim3(64), 0, s, c);
+    else
+      hipLaunchKernelGGL(dkdv_f32_kernel<128>, gk, dim3(64), 0, s, c);
   }
   return hipGetLastError();
 }

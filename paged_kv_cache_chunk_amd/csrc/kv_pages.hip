@@ -120,6 +120,7 @@ hipError_t launch_append(const LayerDev& L, const Geom& g, int elem_bytes, int64
                          int64_t n_tok, const void* k, const void* v, hipStream_t s) {
   const int row_bytes = g.d * elem_bytes;
   const int64_t work = n_tok * g.hkv * (row_bytes / 16);
+  KernelTimer t(KT_APPEND, s);
   hipLaunchKernelGGL(append_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s,
                      (char*)L.k, (char*)L.v, (const char*)k, (const char*)v, L.table, g.hkv,
                      g.page, g.slots, g.max_logical, row_bytes, pos0, n_tok);
@@ -129,6 +130,7 @@ hipError_t launch_append(const LayerDev& L, const Geom& g, int elem_bytes, int64
 hipError_t launch_reps(const LayerDev& L, const Geom& g, bool bf16, int64_t first_page,
                        int64_t n_pages, int64_t length, hipStream_t s) {
   if (n_pages <= 0) return hipSuccess;
+  KernelTimer t(KT_APPEND, s);
   hipLaunchKernelGGL(reps_kernel, dim3((unsigned)n_pages, g.hkv), dim3(g.d), 0, s,
                      (const void*)L.k, L.reps, L.table, g.page, g.slots, g.max_logical, g.d,
                      bf16, first_page, length);

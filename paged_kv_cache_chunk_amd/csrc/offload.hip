@@ -166,6 +166,7 @@ hipError_t launch_fetch_pages(const pkv_pool* p, int layer, int window, bool wit
   const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
   const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
   const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
+  KernelTimer t(KT_FETCH, s);
   hipLaunchKernelGGL(fetch_kernel, dim3((unsigned)n_pages, d.n_kv_heads), dim3(256), 0, s, need,
                      table, d.max_logical_pages, d.n_slots, page_elems, p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
@@ -184,6 +185,7 @@ hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipS
   const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
   const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
   const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
+  KernelTimer t(KT_WRITEBACK, s);
   hipLaunchKernelGGL(writeback_kernel, dim3((unsigned)n_pages, d.n_kv_heads), dim3(256), 0, s,
                      need, table, d.max_logical_pages, d.n_slots, page_elems,
                      d.host_grad_dtype == PKV_BF16, p->m_dk[layer], p->m_dv[layer],

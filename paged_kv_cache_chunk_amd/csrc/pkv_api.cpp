@@ -165,6 +165,14 @@ int64_t pkv_length(const pkv_pool* pool, int32_t layer) {
   return pool->length[layer];
 }
 
+pkv_status pkv_pool_reset(pkv_pool* pool, int32_t layer) {
+  if (!pool) return fail(PKV_EINVAL, "pkv_pool_reset: null pool");
+  if (layer < 0 || layer >= pool->desc.n_layers)
+    return fail(PKV_EINVAL, "pkv_pool_reset: layer %d out of range", layer);
+  pool->length[layer] = 0;
+  return PKV_OK;
+}
+
 pkv_status pkv_page_table_set(pkv_pool* pool, int32_t layer, int32_t kv_head,
                               const int32_t* host_slots, int32_t n) {
   if (!pool || !host_slots) return fail(PKV_EINVAL, "pkv_page_table_set: null argument");

@@ -55,6 +55,23 @@ struct AttnCall {
   float* dq;
 };
 
+// Brackets one kernel launch with timing events when kernel timing is on
+// (pkv_kernel_timing); a no-op otherwise.
+class KernelTimer {
+ public:
+  KernelTimer(int kind, hipStream_t s);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t s_;
+  void* start_;
+};
+
+enum { KT_APPEND = 0, KT_SELECT, KT_FWD, KT_DELTA, KT_DQ, KT_DKDV, KT_FETCH, KT_WRITEBACK, KT_COUNT };
+
 // ---- kernels in kv_pages.hip
 hipError_t launch_append(const LayerDev& L, const Geom& g, int elem_bytes, int64_t pos0,
                          int64_t n_tok, const void* k, const void* v, hipStream_t s);

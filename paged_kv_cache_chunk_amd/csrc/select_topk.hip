@@ -199,6 +199,7 @@ hipError_t launch_select(const LayerDev& L, const Geom& g, bool bf16, int hq, in
   const int first = (int)(q_pos0 / g.page);
   int max_cand = first + nqp - 1 - n_local - n_sink + 1;
   if (max_cand < 1) max_cand = 1;
+  KernelTimer t(KT_SELECT, s);
   float* qbar = scratch;
   float* scores = scratch + (int64_t)nqp * g.hkv * g.d;
   hipLaunchKernelGGL(qmean_kernel, dim3(nqp, g.hkv), dim3(g.d), 0, s, q, qbar, hq, g.hkv, g.d,

@@ -1,0 +1,153 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (whole context, one layer, chunks run in reverse order after every
+append), on outputs the oracle can compute one by one:
+  * O, LSE, dQ of sampled rows (every chunk's first, middle and last row,
+    three query heads);
+  * dK, dV of the last keys of the context in full (only the last rows see
+    them, so the oracle's cost stays small);
+  * for every key, the sums that hold at any size: sum_s dK = 0 and
+    sum_s dV = sum of dO over the group's heads and all rows;
+  * in top-K mode, the selection of sampled chunks (exact, up to the 1e-5
+    score-gap rule) and the sampled rows use the oracle's own selection.
+Inputs come from the GPU generator (synthetic.gpu) and are copied back for
+the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import get_config
+from tests.gpu_util import compare_selection, gpu_available, rel_err, sel_lists
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def _run(cfg, sample_rows, sample_heads, sel_chunks=()):
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, Sparse
+    from synthetic.gpu import GpuWorkload
+
+    w = GpuWorkload(cfg)
+    chunks = [w.chunk(c) for c in range(cfg.n_chunks)]
+    pool = pkv.pkv_pool_create(1, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16)
+    tab = w.table()
+    for g in range(cfg.hkv):
+        pkv.pkv_page_table_set(pool, 0, g, tab[g])
+    sparse = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local) if cfg.sparse else None
+    for ch in chunks:
+        pkv.pkv_append_kv(pool, 0, ch["q_pos0"], ch["k"], ch["v"])
+    samples, sels = {}, {}
+    for c in reversed(range(len(chunks))):
+        ch = chunks[c]
+        n = ch["q"].shape[0]
+        b = ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page, w.dtype, sparse)
+        if sparse is not None:
+            pkv.pkv_select_topk_pages(pool, 0, ch["q_pos0"], ch["q"], sparse.top_k, b.sel[0],
+                                      b.sel[1], sparse.n_sink, sparse.n_local)
+        pkv.pkv_attn_fwd(pool, 0, ch["q_pos0"], ch["q"], b.o, b.lse, cfg.scale, sel=b.sel)
+        pkv.pkv_attn_bwd(pool, 0, ch["q_pos0"], ch["q"], b.o, ch["do"], b.lse, b.dq, cfg.scale,
+                         sel=b.sel)
+        torch.cuda.synchronize()
+        rows = sorted({0, n // 2, n - 1} | set(sample_rows(n)))
+        ri = torch.tensor(rows, device="cuda")
+        samples[c] = dict(rows=rows, O=b.o[ri].float().cpu().numpy(),
+                          lse=b.lse[:, ri].cpu().numpy(), dq=b.dq[ri].cpu().numpy())
+        if sparse is not None and c in sel_chunks:
+            sels[c] = (b.sel[0].cpu().numpy(), b.sel[1].cpu().numpy())
+    N = cfg.n_ctx
+    dk = torch.empty(N, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    pkv.pkv_read_pages(pool, 0, pkv.PKV_DK, dk)
+    pkv.pkv_read_pages(pool, 0, pkv.PKV_DV, dv)
+    torch.cuda.synchronize()
+    host = dict(k=np.concatenate([ch["k"].float().cpu().numpy() for ch in chunks]),
+                v=np.concatenate([ch["v"].float().cpu().numpy() for ch in chunks]))
+    do_sum = [sum(ch["do"].double()[:, g * cfg.group:(g + 1) * cfg.group].sum(dim=(0, 1))
+                  for ch in chunks).cpu().numpy() for g in range(cfg.hkv)]
+    pool.close()
+    return dict(chunks=chunks, samples=samples, sels=sels, dk=dk.cpu().numpy(),
+                dv=dv.cpu().numpy(), do_sum=do_sum, **host)
+
+
+def _oracle_sel(cfg, got, c):
+    ch = got["chunks"][c]
+    q = ch["q"].float().cpu().numpy()
+    return oracle.select_pages(q, got["k"], ch["q_pos0"], cfg.page, cfg.hkv, cfg.top_k,
+                               cfg.n_sink, cfg.n_local, score_dtype=np.float32,
+                               return_scores=True)
+
+
+def _check(cfg, got, heads, key_tail, sel_chunks=()):
+    k, v = got["k"], got["v"]
+    worst = {"O": 0.0, "lse": 0.0, "dq": 0.0}
+    osel = {}
+    for c in sel_chunks:
+        ref_sel, scores = _oracle_sel(cfg, got, c)
+        nd = compare_selection(sel_lists(got["sels"][c]), ref_sel, scores, cfg.top_k)
+        assert nd == 0, f"chunk {c}: {nd} selections differ (inside the score gap)"
+        osel[c] = ref_sel
+    for c, s in got["samples"].items():
+        ch = got["chunks"][c]
+        if cfg.sparse and c not in osel:
+            continue
+        rows = np.array(s["rows"])
+        t_abs = ch["q_pos0"] + rows
+        q = ch["q"].float().cpu().numpy()[rows]
+        do = ch["do"].float().cpu().numpy()[rows]
+        for h in heads:
+            ok = None
+            if cfg.sparse:
+                ok = np.zeros((len(rows), cfg.n_pages), dtype=bool)
+                for n_, r in enumerate(rows):
+                    ok[n_, osel[c][r // cfg.page][h // cfg.group]] = True
+            O, lse, dq = oracle.rows_fwd_bwd(q[:, h], do[:, h], t_abs, h, k, v, cfg.scale,
+                                             cfg.group, cfg.page, ok)
+            worst["O"] = max(worst["O"], rel_err(s["O"][:, h], O))
+            worst["lse"] = max(worst["lse"], rel_err(s["lse"][h], lse))
+            worst["dq"] = max(worst["dq"], rel_err(s["dq"][:, h], dq))
+    N = cfg.n_ctx
+    s0 = N - key_tail
+    last = got["chunks"][-1]
+    off = s0 - last["q_pos0"]
+    sels = None
+    if cfg.sparse:
+        sels = {cfg.n_chunks - 1: osel[cfg.n_chunks - 1]}
+    dk, dv = oracle.key_grads_sampled(s0, last["q"].float().cpu().numpy()[off:],
+                                      last["do"].float().cpu().numpy()[off:], k, v, cfg.scale,
+                                      cfg.chunk, cfg.page, sels)
+    worst["dk_tail"] = rel_err(got["dk"][s0:], dk)
+    worst["dv_tail"] = rel_err(got["dv"][s0:], dv)
+    # sums over every key
+    for g in range(cfg.hkv):
+        sk = np.abs(got["dk"][:, g].astype(np.float64).sum(0)).max()
+        scale_k = np.abs(got["dk"][:, g]).astype(np.float64).sum(0).max()
+        worst[f"sum_dk_{g}"] = sk / scale_k
+        worst[f"sum_dv_{g}"] = rel_err(got["dv"][:, g].astype(np.float64).sum(0), got["do_sum"][g])
+    print(cfg.name, {k_: f"{v_:.2e}" for k_, v_ in worst.items()}, flush=True)
+    for name, e in worst.items():
+        assert e <= 1e-2, f"{name}: {e:.3e}"
+
+
+def test_qwen_32k_dense_full():
+    cfg = get_config("qwen_32k_dense")
+    got = _run(cfg, lambda n: [1, 127, 128, 4095 % n], None)
+    _check(cfg, got, heads=(0, 13, 27), key_tail=64)
+
+
+def test_qwen_128k_dense_full():
+    cfg = get_config("qwen_128k_dense")
+    got = _run(cfg, lambda n: [129], None)
+    _check(cfg, got, heads=(0, 27), key_tail=32)
+
+
+def test_qwen_256k_topk_full():
+    cfg = get_config("qwen_256k_topk")
+    picked = (1, 20, 63)
+    got = _run(cfg, lambda n: [128, 2049], None, sel_chunks=picked)
+    _check(cfg, got, heads=(0, 15), key_tail=32, sel_chunks=picked)
