@@ -106,3 +106,32 @@ def test_bf16_page_table_permutation_invariance():
         assert np.array_equal(a[name], b[name]), name
     for name in ("dk", "dv"):
         assert rel_err(a[name], b[name]) < 1e-5, name
+
+
+def test_bf16_qwen_dense_partial_page_tail():
+    # last chunk of 360 rows: neither a page nor a 32-row tile multiple; the
+    # last page holds 104 tokens
+    cfg = mini_config("qwen_32k_dense", n_ctx=1000, chunk=640)
+    w = Workload(cfg)
+    got = run_layer(cfg, w)
+    _, ref = _oracle_for(cfg, w)
+    _check(cfg, got, ref, TOL["bf16"])
+
+
+def test_bf16_qwen_sparse_partial_page_tail():
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    cfg = mini_config("qwen_256k_topk", n_ctx=2000, chunk=1024, top_k=3)
+    sp = Sparse(top_k=3)
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f, ref = _oracle_for(cfg, w, sp)
+    _check_sel(cfg, f, got, ref, sp)
+    _check(cfg, got, ref, TOL["bf16"])
+
+
+def test_f32_partial_page_tail():
+    cfg = get_config("tiny_f32").replace(n_ctx=500)
+    w = Workload(cfg)
+    got = run_layer(cfg, w)
+    _, ref = _oracle_for(cfg, w)
+    _check(cfg, got, ref, TOL["f32"])
