@@ -41,6 +41,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -71,10 +73,13 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ unsigned bf16_bits(float x) {
-  return (unsigned)__builtin_bit_cast(u16, (__bf16)x);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
-__device__ __forceinline__ unsigned pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
 
 // Raw v_exp_f32 (2^x); arguments are <= 8 or -inf here.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -103,69 +108,103 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int row0, int col0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Copy R rows of 256 bytes into a swizzled LDS tile with NW waves; row r
-// comes from rowptr(r).  One 1 KB global_load_lds per 4 rows.
-template <int R, int NW, typename F>
-__device__ __forceinline__ void dma_tile(char* tile, int w, int lane, F rowptr) {
+// Copy R rows of 256 bytes into a swizzled LDS tile with NW waves: one
+// 1 KB global_load_lds per 4 rows; wave w issues instructions w, w + NW, ..
+// Lane l of instruction u moves 16-byte chunk c = ((64 u + l) % 16) ^ swz(row)
+// of row (64 u + l) / 16, so that it lands at its swizzled place.
+template <int R, int NW>
+struct TileDma {
+  static constexpr int NX = R / 4 / NW;
   static_assert((R / 4) % NW == 0, "rows must split evenly over the waves");
+  int row[NX];       // source row of this lane, per instruction
+  int chunk_b[NX];   // byte offset of its chunk within the row
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int x = 0; x < R / 4 / NW; ++x) {
-    const int u = w + x * NW;
-    const int p = 64 * u + lane;
-    const int row = p >> 4;
-    const int c = (p & 15) ^ swz(row);
-    const char* src = rowptr(row) + (c << 4);
-    __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)(tile + 1024 * u), 16,
-                                     0, 0);
+    for (int x = 0; x < NX; ++x) {
+      const int p = 64 * (w + x * NW) + lane;
+      row[x] = p >> 4;
+      chunk_b[x] = ((p & 15) ^ swz(p >> 4)) << 4;
+    }
   }
-}
+  // rows of `row_bytes` stride starting at base (byte offsets fit 32 bits)
+  __device__ __forceinline__ void issue(char* tile, int w, const char* base, int row_bytes) const {
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const char* src = base + (row[x] * row_bytes + chunk_b[x]);
+      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src,
+                                       (LDS_AS void*)(tile + 1024 * (w + x * NW)), 16, 0, 0);
+    }
+  }
+  // same, with source rows clamped to [0, last_row]
+  __device__ __forceinline__ void issue_clamped(char* tile, int w, const char* base, int row_bytes,
+                                                int last_row) const {
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      const int r = row[x] < last_row ? row[x] : last_row;
+      const char* src = base + (r * row_bytes + chunk_b[x]);
+      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src,
+                                       (LDS_AS void*)(tile + 1024 * (w + x * NW)), 16, 0, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ int sel_count(const AttnCall& c, int il, int g) {
   const int n = c.sel.count[(int64_t)il * c.g.hkv + g];
   return n < 0 ? 0 : (n > c.sel.stride ? c.sel.stride : n);
 }
 
-// Walks the key tiles (BNT keys each) a query block visits: dense = keys
-// 0.. in order; sparse = the pages of the block's selection list, ascending,
-// P / BNT tiles per page.  List entries are clamped into [0, max_logical) so
-// that a malformed selection cannot address outside the pool.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// One key tile: logical page, BNT-row sub-tile inside it, and its first key
+// relative to the chunk's first query.
+struct KeyTile {
+  int pg;
+  int sub;
+  int srel0;
+};
+
+// Walks the key tiles (BNT keys each) a query block visits: dense = pages
+// 0, 1, .. in order; sparse = the pages of the block's selection list,
+// ascending; P / BNT tiles per page.  List entries are clamped into
+// [0, max_logical) so that a malformed selection cannot address outside the
+// pool.  Everything here is wave-uniform and kept in scalar registers.
 template <int BNT>
 struct TileWalk {
   const int32_t* list;  // nullptr: dense
   int tpp;              // tiles per page
   int page;
   int max_logical;
-  int u, sub;           // position of the next tile
-  int64_t dense_next;
-  __device__ __forceinline__ int64_t next() {
-    if (!list) {
-      const int64_t s0 = dense_next;
-      dense_next += BNT;
-      return s0;
+  int rel;              // -q_pos0 (keys relative to the chunk)
+  int u, sub;           // position of the next tile (u: list index or page)
+  __device__ __forceinline__ KeyTile next() {
+    int pg = u;
+    if (list) {
+      pg = list[u];
+      pg = pg < 0 ? 0 : (pg >= max_logical ? max_logical - 1 : pg);
+      pg = uni(pg);
     }
-    int pg = list[u];
-    pg = pg < 0 ? 0 : (pg >= max_logical ? max_logical - 1 : pg);
-    const int64_t s0 = (int64_t)pg * page + (int64_t)sub * BNT;
+    KeyTile t{pg, sub, pg * page + sub * BNT + rel};
     if (++sub == tpp) {
       sub = 0;
       ++u;
     }
-    return s0;
+    return t;
   }
 };
 
-// Tiles of a query block whose last row is at absolute position tmax_blk,
-// and a walker positioned on the first tile.
+// Tiles of a query block whose last row is rlast (relative to q_pos0), and a
+// walker positioned on the first tile.
 template <int BNT>
-__device__ __forceinline__ TileWalk<BNT> make_walk(const AttnCall& c, int g, int r0,
-                                                   int64_t tmax_blk, int* n_tiles) {
+__device__ __forceinline__ TileWalk<BNT> make_walk(const AttnCall& c, int g, int r0, int rlast,
+                                                   int* n_tiles) {
   TileWalk<BNT> W;
   W.list = nullptr;
   W.page = c.g.page;
   W.tpp = c.g.page / BNT;
   W.max_logical = c.g.max_logical;
+  W.rel = (int)(-c.q_pos0);
   W.u = W.sub = 0;
-  W.dense_next = 0;
+  const int64_t tmax_blk = c.q_pos0 + rlast;
   if (!c.sel.pages) {
     *n_tiles = (int)((tmax_blk + BNT) / BNT);
     return W;
@@ -183,16 +222,17 @@ __device__ __forceinline__ TileWalk<BNT> make_walk(const AttnCall& c, int g, int
     while (keep > 0 && base + (int64_t)(keep - 1) * BNT > tmax_blk) --keep;
     n = (n_list - 1) * W.tpp + keep;
   }
-  *n_tiles = n;
+  *n_tiles = uni(n);
   return W;
 }
 
-// Source of row 0 of a key tile starting at absolute key s0 (inside one page).
+// Row 0 of key tile t of KV head g in `pool`.
+template <int BNT>
 __device__ __forceinline__ const char* key_rows(const AttnCall& c, const void* pool, int g,
-                                                int64_t s0) {
-  const int slot = c.L.table[(int64_t)g * c.g.max_logical + s0 / c.g.page];
+                                                const KeyTile& t) {
+  const int slot = uni(c.L.table[(int64_t)g * c.g.max_logical + t.pg]);
   return reinterpret_cast<const char*>(pool) +
-         (((int64_t)g * c.g.slots + slot) * c.g.page + s0 % c.g.page) * ROWB;
+         (((int64_t)g * c.g.slots + slot) * c.g.page + t.sub * BNT) * ROWB;
 }
 
 __device__ __forceinline__ void wait_dma_and_sync() {
@@ -209,14 +249,13 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   constexpr int MT = BNT / 32;        // 32-key m-tiles per tile
   constexpr int TB = BNT * ROWB;      // bytes per K or V tile
   __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int qb = n_qblocks - 1 - (int)blockIdx.x;  // longest rows first
   const int h = blockIdx.y;
-  const int G = c.hq / c.g.hkv, g = h / G;
+  const int G = c.hq / c.g.hkv, g = uni(h / G);
   const int r0 = qb * BM;
   const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
-  const int64_t tmax_blk = c.q_pos0 + rlast;
   const int rw0 = r0 + 32 * NT * w;   // wave's first row (relative to q_pos0)
   const int tw_min = rw0 < rlast ? rw0 : rlast;
   const int tw_max = rw0 + 32 * NT - 1 < rlast ? rw0 + 32 * NT - 1 : rlast;
@@ -234,12 +273,12 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   }
 
   int n_tiles;
-  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, tmax_blk, &n_tiles);
-  auto issue = [&](int b, int64_t s0) {
-    const char* kb = key_rows(c, c.L.k, g, s0);
-    const char* vb = key_rows(c, c.L.v, g, s0);
-    dma_tile<BNT, NW>(sm[b], w, lane, [&](int r) { return kb + r * ROWB; });
-    dma_tile<BNT, NW>(sm[b] + TB, w, lane, [&](int r) { return vb + r * ROWB; });
+  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, rlast, &n_tiles);
+  TileDma<BNT, NW> dma;
+  dma.init(w, lane);
+  auto issue = [&](int b, const KeyTile& t) {
+    dma.issue(sm[b], w, key_rows<BNT>(c, c.L.k, g, t), ROWB);
+    dma.issue(sm[b] + TB, w, key_rows<BNT>(c, c.L.v, g, t), ROWB);
   };
 
   f32x16 oacc[4][NT];
@@ -253,23 +292,23 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   }
   const float c2 = c.scale * kLog2e;
 
-  int64_t s_cur = 0;
+  KeyTile t_cur{0, 0, 0};
   if (n_tiles > 0) {
-    s_cur = walk.next();
-    issue(0, s_cur);
+    t_cur = walk.next();
+    issue(0, t_cur);
   }
   wait_dma_and_sync();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int b = j & 1;
-    int64_t s_next = 0;
+    KeyTile t_next{0, 0, 0};
     if (j + 1 < n_tiles) {
-      s_next = walk.next();
-      issue(b ^ 1, s_next);
+      t_next = walk.next();
+      issue(b ^ 1, t_next);
     }
     const char* kt = sm[b];
     const char* vt = sm[b] + TB;
-    const int srel0 = (int)(s_cur - c.q_pos0);  // tile's first key, relative to q_pos0
+    const int srel0 = t_cur.srel0;  // tile's first key, relative to q_pos0
     if (srel0 <= tw_max) {
       f32x16 sacc[MT][NT];
 #pragma unroll
@@ -346,7 +385,7 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
         }
       }
     }
-    s_cur = s_next;
+    t_cur = t_next;
     wait_dma_and_sync();
   }
 
@@ -379,14 +418,13 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   constexpr int MT = BNT / 32;
   constexpr int TB = BNT * ROWB;
   __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int qb = n_qblocks - 1 - (int)blockIdx.x;
   const int h = blockIdx.y;
-  const int G = c.hq / c.g.hkv, g = h / G;
+  const int G = c.hq / c.g.hkv, g = uni(h / G);
   const int r0 = qb * BM;
   const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
-  const int64_t tmax_blk = c.q_pos0 + rlast;
   const int rw0 = r0 + 32 * NT * w;
   const int tw_min = rw0 < rlast ? rw0 : rlast;
   const int tw_max = rw0 + 32 * NT - 1 < rlast ? rw0 + 32 * NT - 1 : rlast;
@@ -407,18 +445,18 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
       qf[nt][ks] = as_bf16x8(ld16(qrow + 16 * ks));
       df[nt][ks] = as_bf16x8(ld16(drow + 16 * ks));
     }
-    lse2[nt] = c.lse_in[(int64_t)h * c.n_q + r] * kLog2e;
+    lse2[nt] = c.lse2[(int64_t)h * c.n_q + r];
     Dl[nt] = c.delta[(int64_t)h * c.n_q + r];
   }
   const float c2 = c.scale * kLog2e;
 
   int n_tiles;
-  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, tmax_blk, &n_tiles);
-  auto issue = [&](int b, int64_t s0) {
-    const char* kb = key_rows(c, c.L.k, g, s0);
-    const char* vb = key_rows(c, c.L.v, g, s0);
-    dma_tile<BNT, NW>(sm[b], w, lane, [&](int r) { return kb + r * ROWB; });
-    dma_tile<BNT, NW>(sm[b] + TB, w, lane, [&](int r) { return vb + r * ROWB; });
+  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, rlast, &n_tiles);
+  TileDma<BNT, NW> dma;
+  dma.init(w, lane);
+  auto issue = [&](int b, const KeyTile& t) {
+    dma.issue(sm[b], w, key_rows<BNT>(c, c.L.k, g, t), ROWB);
+    dma.issue(sm[b] + TB, w, key_rows<BNT>(c, c.L.v, g, t), ROWB);
   };
 
   f32x16 qacc[4][NT];
@@ -427,23 +465,23 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) qacc[dt][nt] = f32x16{};
 
-  int64_t s_cur = 0;
+  KeyTile t_cur{0, 0, 0};
   if (n_tiles > 0) {
-    s_cur = walk.next();
-    issue(0, s_cur);
+    t_cur = walk.next();
+    issue(0, t_cur);
   }
   wait_dma_and_sync();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int b = j & 1;
-    int64_t s_next = 0;
+    KeyTile t_next{0, 0, 0};
     if (j + 1 < n_tiles) {
-      s_next = walk.next();
-      issue(b ^ 1, s_next);
+      t_next = walk.next();
+      issue(b ^ 1, t_next);
     }
     const char* kt = sm[b];
     const char* vt = sm[b] + TB;
-    const int srel0 = (int)(s_cur - c.q_pos0);
+    const int srel0 = t_cur.srel0;
     if (srel0 <= tw_max) {
       f32x16 sacc[MT][NT], pacc[MT][NT];
 #pragma unroll
@@ -507,7 +545,7 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
         }
       }
     }
-    s_cur = s_next;
+    t_cur = t_next;
     wait_dma_and_sync();
   }
 
@@ -533,20 +571,22 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // -------------------------------------------------------------------- dK/dV
+template <int BQT>
 struct __align__(1024) DkvSmem {
-  char q[2][BQ * ROWB];
-  char o[2][BQ * ROWB];
-  float lsd[2][2 * BQ];  // per buffer: LSE of the 32 rows, then D of the 32 rows
+  char q[2][BQT * ROWB];
+  char o[2][BQT * ROWB];
+  float lsd[2][2 * BQT];  // per buffer: LSE of the BQT rows, then D of the BQT rows
   int qpl[1024];
   int n_qpl;
 };
 
-// grid (ceil(n_keys / 128), hkv, splits); OCC: waves per SIMD the register
-// budget is sized for.
-template <int OCC>
+// grid (ceil(n_keys / 128), hkv, splits).  BQT: query rows per tile (32 or
+// 64); OCC: waves per SIMD the register budget is sized for.
+template <int OCC, int BQT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 dkdv_bf16_kernel(AttnCall c, int splits) {
-  __shared__ DkvSmem sm;
+  constexpr int ST = BQT / 32;  // 32-row sub-tiles per tile
+  __shared__ DkvSmem<BQT> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int g = blockIdx.y;
@@ -558,9 +598,9 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   const int64_t wk0 = s_base + 32 * w;            // this wave's first key
   const int s_rel = (int)(wk0 + l32 - c.q_pos0);  // this lane's key, relative to q_pos0
   const int nqp = (c.n_q + P - 1) / P;
-  const int tiles_pp = P / BQ;
+  const int tiles_pp = P / BQT;
 
-  // Row tiles (32 query rows) of the chunk that can see this key slab.
+  // Row tiles (BQT query rows) of the chunk that can see this key slab.
   int n_rt, r_first = 0;
   if (c.sel.pages) {
     if (tid == 0) {
@@ -582,8 +622,8 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   } else {
     r_first = (int)(s_base - c.q_pos0);
     if (r_first < 0) r_first = 0;
-    r_first -= r_first % BQ;
-    n_rt = (c.n_q - r_first + BQ - 1) / BQ;
+    r_first -= r_first % BQT;
+    n_rt = (c.n_q - r_first + BQT - 1) / BQT;
   }
   const int total = n_rt * G;
   const int it0 = (int)((int64_t)total * blockIdx.z / splits);
@@ -591,7 +631,7 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   if (it0 >= it1) return;
 
   bf16x8 kf[8], vf[8];
-  const int slot = c.L.table[(int64_t)g * c.g.max_logical + kpage];
+  const int slot = uni(c.L.table[(int64_t)g * c.g.max_logical + kpage]);
   const int64_t prow = ((int64_t)g * c.g.slots + slot) * P + ((wk0 + l32) % P);
   {
     const u16* kr = reinterpret_cast<const u16*>(c.L.k) + prow * D + 8 * half;
@@ -613,30 +653,38 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   auto tile_row0 = [&](int it, int* hh) -> int {
     *hh = g * G + it / n_rt;
     const int rt = it % n_rt;
-    if (c.sel.pages) return sm.qpl[rt / tiles_pp] * P + (rt % tiles_pp) * BQ;
-    return r_first + rt * BQ;
+    if (c.sel.pages) return sm.qpl[rt / tiles_pp] * P + (rt % tiles_pp) * BQT;
+    return r_first + rt * BQT;
   };
   // Q and dO rows of the tile straight into LDS (rows past the chunk repeat its
-  // last row and are masked); the 32 LSE and 32 D values by wave 0.
+  // last row and are masked); log2-scaled LSE and D of the rows by wave 0.
+  TileDma<BQT, 4> dma;
+  dma.init(w, lane);
+  const int qrow_b = c.hq * ROWB;
   auto issue = [&](int b, int it) {
     int hh;
     const int row0 = tile_row0(it, &hh);
-    const char* qb = reinterpret_cast<const char*>(c.q);
-    const char* ob = reinterpret_cast<const char*>(c.dout);
-    dma_tile<BQ, 4>(sm.q[b], w, lane, [&](int r) {
-      const int rr = row0 + r < c.n_q ? row0 + r : c.n_q - 1;
-      return qb + ((int64_t)rr * c.hq + hh) * ROWB;
-    });
-    dma_tile<BQ, 4>(sm.o[b], w, lane, [&](int r) {
-      const int rr = row0 + r < c.n_q ? row0 + r : c.n_q - 1;
-      return ob + ((int64_t)rr * c.hq + hh) * ROWB;
-    });
+    const int64_t off = ((int64_t)row0 * c.hq + hh) * ROWB;
+    const char* qb = reinterpret_cast<const char*>(c.q) + off;
+    const char* ob = reinterpret_cast<const char*>(c.dout) + off;
+    if (row0 + BQT <= c.n_q) {
+      dma.issue(sm.q[b], w, qb, qrow_b);
+      dma.issue(sm.o[b], w, ob, qrow_b);
+    } else {
+      dma.issue_clamped(sm.q[b], w, qb, qrow_b, c.n_q - 1 - row0);
+      dma.issue_clamped(sm.o[b], w, ob, qrow_b, c.n_q - 1 - row0);
+    }
     if (w == 0) {
-      const int rr = row0 + l32;
-      const int rc = rr < c.n_q ? rr : c.n_q - 1;
-      const float* src = half == 0 ? c.lse_in + (int64_t)hh * c.n_q + rc
-                                   : c.delta + (int64_t)hh * c.n_q + rc;
-      __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)sm.lsd[b], 4, 0, 0);
+#pragma unroll
+      for (int x = 0; x < BQT / 32; ++x) {  // 64 values per instruction
+        const int v = 64 * x + lane;         // value index in lsd[b]
+        const bool is_d = v >= BQT;
+        const int rr = row0 + (is_d ? v - BQT : v);
+        const int rc = rr < c.n_q ? rr : c.n_q - 1;
+        const float* src = (is_d ? c.delta : c.lse2) + (int64_t)hh * c.n_q + rc;
+        __builtin_amdgcn_global_load_lds((const GLB_AS void*)src, (LDS_AS void*)(sm.lsd[b] + 64 * x),
+                                         4, 0, 0);
+      }
     }
   };
 
@@ -648,57 +696,75 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
     int hh;
     const int row0 = tile_row0(it, &hh);
     const int64_t t_min = c.q_pos0 + row0;
-    const int64_t t_max = t_min + BQ - 1;
+    const int64_t t_max = t_min + BQT - 1;
     if (wk0 <= t_max) {
       const char* qt = sm.q[b];
       const char* ot = sm.o[b];
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 sacc[ST], pacc[ST];
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        sacc[st] = f32x16{};
+        pacc[st] = f32x16{};
+      }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc = mfma(frag_row(qt, l32, ks, half), kf[ks], sacc);
-        pacc = mfma(frag_row(ot, l32, ks, half), vf[ks], pacc);
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+          sacc[st] = mfma(frag_row(qt, 32 * st + l32, ks, half), kf[ks], sacc[st]);
+          pacc[st] = mfma(frag_row(ot, 32 * st + l32, ks, half), vf[ks], pacc[st]);
+        }
       }
       // keys past a row (causal) and rows past the chunk get probability 0
-      const bool need_mask = (wk0 + 31 > t_min) || (row0 + BQ > c.n_q);
       const float* lse_b = sm.lsd[b];
-      const float* dl_b = sm.lsd[b] + BQ;
+      const float* dl_b = sm.lsd[b] + BQT;
+      auto pass = [&](auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // rows 16 kk .. 16 kk + 15 of the tile: accumulator entries 8 kk .. 8 kk + 7
-        float p[8], ds[8];
+        for (int kk = 0; kk < 2 * ST; ++kk) {
+          // tile rows 16 kk .. 16 kk + 15: sub-tile kk / 2, entries 8 (kk % 2) ..
+          const int st = kk >> 1;
+          float p[8], ds[8];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j4 = 2 * kk + jj;
-          const float4 L4 = *reinterpret_cast<const float4*>(lse_b + 8 * j4 + 4 * half);
-          const float4 D4 = *reinterpret_cast<const float4*>(dl_b + 8 * j4 + 4 * half);
-          const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-          const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j4 = 2 * (kk & 1) + jj;
+            const int rb = 32 * st + 8 * j4 + 4 * half;  // first of the 4 rows
+            const float4 L4 = *reinterpret_cast<const float4*>(lse_b + rb);
+            const float4 D4 = *reinterpret_cast<const float4*>(dl_b + rb);
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+            const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int tr = row0 + 8 * j4 + 4 * half + x;
-            float sv = sacc[4 * j4 + x];
-            if (need_mask && (s_rel > tr || tr >= c.n_q)) sv = -INFINITY;
-            const float pr = ex2(fmaf(sv, c2, -Lr[x] * kLog2e));
-            p[4 * jj + x] = pr;
-            ds[4 * jj + x] = pr * (pacc[4 * j4 + x] - Dr[x]);
+            for (int x = 0; x < 4; ++x) {
+              float sv = sacc[st][4 * j4 + x];
+              if (MASK) {
+                const int tr = row0 + rb + x;
+                if (s_rel > tr || tr >= c.n_q) sv = -INFINITY;
+              }
+              const float pr = ex2(fmaf(sv, c2, -Lr[x]));
+              p[4 * jj + x] = pr;
+              ds[4 * jj + x] = pr * (pacc[st][4 * j4 + x] - Dr[x]);
+            }
+          }
+          u32x4 pv, dv;
+          pv.x = pack2(p[0], p[1]);
+          pv.y = pack2(p[2], p[3]);
+          pv.z = pack2(p[4], p[5]);
+          pv.w = pack2(p[6], p[7]);
+          dv.x = pack2(ds[0], ds[1]);
+          dv.y = pack2(ds[2], ds[3]);
+          dv.z = pack2(ds[4], ds[5]);
+          dv.w = pack2(ds[6], ds[7]);
+          const bf16x8 pa = as_bf16x8(pv), da = as_bf16x8(dv);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            vacc[dt] = mfma(pa, frag_tr(ot, 16 * kk, 32 * dt, lane), vacc[dt]);
+            kacc[dt] = mfma(da, frag_tr(qt, 16 * kk, 32 * dt, lane), kacc[dt]);
           }
         }
-        u32x4 pv, dv;
-        pv.x = pack2(p[0], p[1]);
-        pv.y = pack2(p[2], p[3]);
-        pv.z = pack2(p[4], p[5]);
-        pv.w = pack2(p[6], p[7]);
-        dv.x = pack2(ds[0], ds[1]);
-        dv.y = pack2(ds[2], ds[3]);
-        dv.z = pack2(ds[4], ds[5]);
-        dv.w = pack2(ds[6], ds[7]);
-        const bf16x8 pa = as_bf16x8(pv), da = as_bf16x8(dv);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          vacc[dt] = mfma(pa, frag_tr(ot, 16 * kk, 32 * dt, lane), vacc[dt]);
-          kacc[dt] = mfma(da, frag_tr(qt, 16 * kk, 32 * dt, lane), kacc[dt]);
-        }
-      }
+      };
+      if ((wk0 + 31 > t_min) || (row0 + BQT > c.n_q))
+        pass(std::true_type{});
+      else
+        pass(std::false_type{});
     }
     wait_dma_and_sync();
   }
@@ -774,14 +840,21 @@ hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
   int splits = (2048 + n_slabs * c.g.hkv - 1) / (n_slabs * c.g.hkv);
   if (splits < 1) splits = 1;
   if (splits > 16) splits = 16;
-  static const int occ = getenv("PKV_DKDV_OCC") && !strcmp(getenv("PKV_DKDV_OCC"), "2") ? 2 : 1;
+  // PKV_DKDV: "1x32" (one wave per SIMD, 32-row query tiles), "1x64", "2x32"
+  static const int kind = [] {
+    const char* v = getenv("PKV_DKDV");
+    if (v && !strcmp(v, "1x32")) return 0;
+    if (v && !strcmp(v, "2x32")) return 2;
+    return 1;
+  }();
   KernelTimer t(KT_DKDV, s);
-  if (occ == 2)
-    hipLaunchKernelGGL(dkdv_bf16_kernel<2>, dim3(n_slabs, c.g.hkv, splits), dim3(256), 0, s, c,
-                       splits);
+  const dim3 grid(n_slabs, c.g.hkv, splits);
+  if (kind == 0)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<1, 32>), grid, dim3(256), 0, s, c, splits);
+  else if (kind == 2)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<2, 32>), grid, dim3(256), 0, s, c, splits);
   else
-    hipLaunchKernelGGL(dkdv_bf16_kernel<1>, dim3(n_slabs, c.g.hkv, splits), dim3(256), 0, s, c,
-                       splits);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<1, 64>), grid, dim3(256), 0, s, c, splits);
   return hipGetLastError();
 }
 

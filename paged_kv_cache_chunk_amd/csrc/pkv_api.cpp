@@ -303,7 +303,7 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   if (cdiv(n_q, pool->desc.page_size) > 1024)
     return fail(PKV_EUNSUPPORTED, "pkv_attn_bwd: chunks of more than 1024 pages");
   if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes,
-                           (int64_t)n_q_heads * n_q * (int64_t)sizeof(float))) != PKV_OK)
+                           2 * (int64_t)n_q_heads * n_q * (int64_t)sizeof(float))) != PKV_OK)
     return st;
   if ((st = pool_before_compute(pool, layer, stream)) != PKV_OK) return st;
   AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
@@ -313,6 +313,7 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   c.lse_in = lse;
   c.dq = dq;
   c.delta = (float*)pool->d_delta;
+  c.lse2 = pool->desc.kv_dtype == PKV_BF16 ? c.delta + (int64_t)n_q_heads * n_q : nullptr;
   hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_bwd_bf16(c, stream) : launch_bwd_f32(c, stream);
   if (e != hipSuccess) return hip_fail(e, "pkv_attn_bwd: launch");
   return pool_after_compute(pool, layer, stream);

@@ -52,6 +52,7 @@ struct AttnCall {
   float* lse;
   const float* lse_in;
   float* delta;  // D = rowsum(dO * O), [hq][n_q]
+  float* lse2;   // lse * log2(e), [hq][n_q] (bf16 backward only)
   float* dq;
 };
 
