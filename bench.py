@@ -208,7 +208,21 @@ def main():
                     help="second workload in the same line ('none' to skip)")
     ap.add_argument("--cpu-rows", type=int, default=64,
                     help="query rows in the oracle's CPU sample (0 skips it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (reference "
+                         "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "

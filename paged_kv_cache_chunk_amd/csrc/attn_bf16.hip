@@ -251,9 +251,14 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int qb = n_qblocks - 1 - (int)blockIdx.x;  // longest rows first
-  const int h = blockIdx.y;
-  const int G = c.hq / c.g.hkv, g = uni(h / G);
+  // Workgroup -> (query block, head): workgroups are dealt to the 8 XCDs
+  // round-robin, so bid % Hkv = KV head keeps every head's workgroups on the
+  // same XCDs (sharing their L2 for that head's K/V); longest rows first.
+  const int G = c.hq / c.g.hkv;
+  const int bid = blockIdx.x;
+  const int g = uni(bid % c.g.hkv), m = uni(bid / c.g.hkv);
+  const int qb = n_qblocks - 1 - m / G;
+  const int h = g * G + m % G;
   const int r0 = qb * BM;
   const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
   const int rw0 = r0 + 32 * NT * w;   // wave's first row (relative to q_pos0)
@@ -420,9 +425,11 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int qb = n_qblocks - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y;
-  const int G = c.hq / c.g.hkv, g = uni(h / G);
+  const int G = c.hq / c.g.hkv;
+  const int bid = blockIdx.x;
+  const int g = uni(bid % c.g.hkv), m = uni(bid / c.g.hkv);
+  const int qb = n_qblocks - 1 - m / G;
+  const int h = g * G + m % G;
   const int r0 = qb * BM;
   const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
   const int rw0 = r0 + 32 * NT * w;
@@ -580,7 +587,7 @@ struct __align__(1024) DkvSmem {
   int n_qpl;
 };
 
-// grid (ceil(n_keys / 128), hkv, splits).  BQT: query rows per tile (32 or
+// grid ceil(n_keys / 128) * hkv * splits.  BQT: query rows per tile (32 or
 // 64); OCC: waves per SIMD the register budget is sized for.
 template <int OCC, int BQT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
@@ -589,11 +596,17 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   __shared__ DkvSmem<BQT> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int g = blockIdx.y;
+  // Workgroup -> (KV head, slab, split): bid % Hkv = KV head keeps a head's
+  // workgroups on the same XCDs; the earliest slabs (the most query rows)
+  // first.
+  const int bid = blockIdx.x;
+  const int g = bid % c.g.hkv;
+  const int m = bid / c.g.hkv;
+  const int slab = m / splits, zsplit = m % splits;
   const int G = c.hq / c.g.hkv;
   const int P = c.g.page;
   const int64_t n_keys = c.q_pos0 + c.n_q;
-  const int64_t s_base = (int64_t)blockIdx.x * 128;
+  const int64_t s_base = (int64_t)slab * 128;
   const int64_t kpage = s_base / P;
   const int64_t wk0 = s_base + 32 * w;            // this wave's first key
   const int s_rel = (int)(wk0 + l32 - c.q_pos0);  // this lane's key, relative to q_pos0
@@ -626,8 +639,8 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
     n_rt = (c.n_q - r_first + BQT - 1) / BQT;
   }
   const int total = n_rt * G;
-  const int it0 = (int)((int64_t)total * blockIdx.z / splits);
-  const int it1 = (int)((int64_t)total * (blockIdx.z + 1) / splits);
+  const int it0 = (int)((int64_t)total * zsplit / splits);
+  const int it1 = (int)((int64_t)total * (zsplit + 1) / splits);
   if (it0 >= it1) return;
 
   bf16x8 kf[8], vf[8];
@@ -804,13 +817,13 @@ hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s) {
   KernelTimer t(KT_FWD, s);
   switch (choice) {
     case 1:
-      hipLaunchKernelGGL((fwd_bf16_kernel<2, 32>), dim3(nqb, c.hq), dim3(128), 0, s, c, nqb);
+      hipLaunchKernelGGL((fwd_bf16_kernel<2, 32>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
       break;
     case 2:
-      hipLaunchKernelGGL((fwd_bf16_kernel<2, 64>), dim3(nqb, c.hq), dim3(128), 0, s, c, nqb);
+      hipLaunchKernelGGL((fwd_bf16_kernel<2, 64>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
       break;
     default:
-      hipLaunchKernelGGL((fwd_bf16_kernel<1, 64>), dim3(nqb, c.hq), dim3(256), 0, s, c, nqb);
+      hipLaunchKernelGGL((fwd_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
   }
   return hipGetLastError();
 }
@@ -824,13 +837,13 @@ hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
     KernelTimer t(KT_DQ, s);
     switch (choice) {
       case 1:
-        hipLaunchKernelGGL((dq_bf16_kernel<2, 32>), dim3(nqb, c.hq), dim3(128), 0, s, c, nqb);
+        hipLaunchKernelGGL((dq_bf16_kernel<2, 32>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
         break;
       case 2:
-        hipLaunchKernelGGL((dq_bf16_kernel<2, 64>), dim3(nqb, c.hq), dim3(128), 0, s, c, nqb);
+        hipLaunchKernelGGL((dq_bf16_kernel<2, 64>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
         break;
       default:
-        hipLaunchKernelGGL((dq_bf16_kernel<1, 64>), dim3(nqb, c.hq), dim3(256), 0, s, c, nqb);
+        hipLaunchKernelGGL((dq_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
     }
     e = hipGetLastError();
   }
@@ -848,7 +861,7 @@ hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
     return 1;
   }();
   KernelTimer t(KT_DKDV, s);
-  const dim3 grid(n_slabs, c.g.hkv, splits);
+  const dim3 grid(n_slabs * c.g.hkv * splits);
   if (kind == 0)
     hipLaunchKernelGGL((dkdv_bf16_kernel<1, 32>), grid, dim3(256), 0, s, c, splits);
   else if (kind == 2)
