@@ -198,6 +198,118 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
+def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
+    """Host-offloaded stack: every layer's K/V and KV-gradient pools in pinned
+    host memory (bf16), an HBM window of two layers, the next layer's
+    selected pages prefetched on a side stream during the current layer, and
+    gradient pages written back asynchronously.  Times the backward sweep
+    (chunks last to first, layers last to first: select + prefetch + forward
+    + backward + writeback); the forward sweep that appends every chunk's
+    K/V to the host tier is untimed setup."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
+    from synthetic.gpu import GpuWorkload
+
+    L = cfg.n_layers
+    ws = [GpuWorkload(cfg, layer=l) for l in range(L)]
+    sp = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local) if cfg.sparse else None
+    results = {}
+    modes = [("offload", 1)] + ([("resident", 0)] if resident_ab else [])
+    for mode, host_tier in modes:
+        t0 = time.time()
+        pool = pkv.pkv_pool_create(L, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
+                                   pkv.PKV_BF16, host_tier=host_tier, host_grad_dtype=pkv.PKV_BF16,
+                                   device_budget_bytes=cfg.hbm_cap_bytes if host_tier else 0)
+        dev_b, host_b = pkv.pkv_pool_bytes(pool)
+        for l in range(L):
+            tab = ws[l].table()
+            for g in range(cfg.hkv):
+                pkv.pkv_page_table_set(pool, l, g, tab[g])
+        log(f"[bench] {cfg.name} {mode}: pool created in {time.time() - t0:.1f}s "
+            f"(HBM {dev_b / 2**30:.2f} GiB, pinned host {host_b / 2**30:.2f} GiB)")
+        t0 = time.time()
+        for c in range(cfg.n_chunks):
+            for l in range(L):
+                kv = ws[l].chunk(c, "kv")
+                pkv.pkv_append_kv(pool, l, kv["q_pos0"], kv["k"], kv["v"])
+            if c % 16 == 15:
+                torch.cuda.synchronize()
+                log(f"[bench] {cfg.name} {mode}: appended chunk {c + 1}/{cfg.n_chunks}")
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name} {mode}: forward-sweep appends in {time.time() - t0:.1f}s")
+        sweep = OffloadSweep(pool, L, cfg.hq, cfg.hkv, cfg.d, cfg.page, cfg.scale, sp,
+                             torch.bfloat16)
+        bufsets = {}
+
+        def inputs(l, c):
+            return ws[l].chunk(c, "qd")
+
+        chunk_ids = list(reversed(range(cfg.n_chunks)))[:steps] if steps > 0 else \
+            list(reversed(range(cfg.n_chunks)))
+        pkv.pkv_kernel_timing(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for n_done, c in enumerate(chunk_ids):
+            n = cfg.chunk_range(c)[1]
+            if n not in bufsets:
+                bufsets[n] = {l: ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page,
+                                              torch.bfloat16, sp) for l in range(2)}
+            bufs = {l: bufsets[n][l % 2] for l in range(L)}
+            sweep.chunk(c, inputs, bufs)
+            if n_done % 8 == 7:
+                torch.cuda.synchronize()
+                log(f"[bench] {cfg.name} {mode}: backward sweep chunk {n_done + 1}/"
+                    f"{len(chunk_ids)}, {time.perf_counter() - t0:.1f}s")
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kt = pkv.pkv_kernel_times()
+        pkv.pkv_kernel_timing(False)
+        fetched, written = pkv.pkv_offload_bytes(pool)
+        compute = sum(kt[k][0] for k in ("select", "fwd", "delta", "dq", "dkdv")) / 1e3
+        copy = sum(kt[k][0] for k in ("fetch", "writeback")) / 1e3
+        results[mode] = {"wall_s": wall, "compute_kernels_s": compute, "copy_kernels_s": copy,
+                         "fetched_bytes": fetched, "written_bytes": written,
+                         "chunks": len(chunk_ids), "hbm_bytes": dev_b, "host_bytes": host_b,
+                         "kernels": {k: round(v[0], 1) for k, v in kt.items() if v[1]}}
+        log(f"[bench] {cfg.name} {mode}: {results[mode]}")
+        pool.close()
+        torch.cuda.empty_cache()
+    off = results["offload"]
+    tokens = sum(cfg.chunk_range(c)[1] for c in (list(reversed(range(cfg.n_chunks)))[:steps]
+                                                  if steps > 0 else range(cfg.n_chunks)))
+    out = {
+        "workload": f"{cfg.name}: {L} layers, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, top-K "
+                    f"{cfg.top_k} + {cfg.n_sink} sink + {cfg.n_local} local pages, K/V and "
+                    f"gradient pools in pinned host memory (bf16), HBM window of 2 layers",
+        "chunks_timed": off["chunks"],
+        "tokens_per_s_per_layer": round(tokens * L / off["wall_s"], 1),
+        "backward_sweep_s": round(off["wall_s"], 3),
+        "compute_kernels_s": round(off["compute_kernels_s"], 3),
+        "copy_kernels_s": round(off["copy_kernels_s"], 3),
+        # host link busy time: fetches (host -> HBM) and writebacks (HBM -> host)
+        # run on two streams, one per direction of the link
+        "link_s": round(max(off["kernels"].get("fetch", 0), off["kernels"].get("writeback", 0)) / 1e3, 3),
+        "fetched_gb": round(off["fetched_bytes"] / 1e9, 3),
+        "written_back_gb": round(off["written_bytes"] / 1e9, 3),
+        "fetch_gbs": round(off["fetched_bytes"] / 1e9 / max(off["kernels"].get("fetch", 0) / 1e3, 1e-9), 1),
+        "writeback_gbs": round(off["written_bytes"] / 1e9 / max(off["kernels"].get("writeback", 0) / 1e3, 1e-9), 1),
+        "hbm_gib": round(off["hbm_bytes"] / 2**30, 3),
+        "host_gib": round(off["host_bytes"] / 2**30, 3),
+        "kernels_ms": off["kernels"],
+    }
+    if "resident" in results:
+        res_s = results["resident"]["wall_s"]
+        link = out["link_s"]
+        out["resident_s"] = round(res_s, 3)
+        out["offload_overhead"] = round(off["wall_s"] / res_s - 1, 4)
+        # share of the link time hidden behind compute, and the most that
+        # could be hidden (all compute overlapped): min(1, resident / link)
+        out["overlap"] = round(max(0.0, (link - (off["wall_s"] - res_s)) / max(link, 1e-9)), 4)
+        out["overlap_bound"] = round(min(1.0, res_s / max(link, 1e-9)), 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +320,12 @@ def main():
                     help="second workload in the same line ('none' to skip)")
     ap.add_argument("--cpu-rows", type=int, default=64,
                     help="query rows in the oracle's CPU sample (0 skips it)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="offloaded workload: number of layers (default: the config's)")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="offloaded workload: time only the last N chunks of the backward sweep")
+    ap.add_argument("--resident-ab", action="store_true",
+                    help="offloaded workload: also run the same sweep with all pools in HBM")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -237,6 +355,14 @@ def main():
         sys.exit(1)
 
     cfg = get_config(args.workload)
+    if cfg.host_tier:
+        if args.layers:
+            cfg = cfg.replace(n_layers=args.layers)
+        res = offload_bench(cfg, args.chunks, args.resident_ab)
+        res.update({"metric": "offloaded top-K stack: backward-sweep tokens/s per layer",
+                    "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(res), flush=True)
+        return
     lb = LayerBench(cfg)
     log(f"[bench] {cfg.name}: warmup {args.warmup}, timing {args.steps} steps")
     ms, kt = lb.run(args.steps, args.warmup)

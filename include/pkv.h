@@ -227,6 +227,12 @@ pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
 pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_stream,
                                hipEvent_t done);
 
+/* Host-tier pools: total bytes moved so far by pkv_prefetch_pages (host ->
+ * HBM, K/V and gradients) and by pkv_writeback_grads (HBM -> host), counted
+ * on the device by the copy kernels.  Synchronises the device.  Both are 0
+ * without a host tier. */
+pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written);
+
 /* Zero the dK/dV pool of `layer` (all slots; the host tier too in host-tier
  * mode, synchronously). */
 pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);

@@ -26,7 +26,7 @@ EXPORTS = (
     "pkv_append_kv", "pkv_attn_fwd", "pkv_attn_bwd", "pkv_select_topk_pages",
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
     "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
-    "pkv_kernel_times",
+    "pkv_kernel_times", "pkv_offload_bytes",
 )
 KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "pkv_read_pages": [P, I32, I32, VP, VP],
             "pkv_pool_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
             "pkv_pool_reset": [P, I32],
+            "pkv_offload_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
             "pkv_kernel_timing": [I32],
             "pkv_kernel_times": [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)],
         }
@@ -230,6 +231,13 @@ def pkv_read_pages(pool: Pool, layer: int, what: int, dst, stream=None) -> None:
 def pkv_pool_bytes(pool: Pool) -> tuple[int, int]:
     a, b = ctypes.c_int64(), ctypes.c_int64()
     _check(lib().pkv_pool_bytes(pool.handle, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def pkv_offload_bytes(pool: Pool) -> tuple[int, int]:
+    """(bytes fetched host->HBM, bytes written back HBM->host) so far."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().pkv_offload_bytes(pool.handle, ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
 
 

@@ -57,3 +57,74 @@ def chunk_step(pool: Pool, layer: int, q_pos0: int, q, do, o, lse, dq, scale: fl
     if forward:
         pkv_attn_fwd(pool, layer, q_pos0, q, o, lse, scale, sel=sel, stream=stream)
     pkv_attn_bwd(pool, layer, q_pos0, q, o, do, lse, dq, scale, sel=sel, stream=stream)
+
+
+class OffloadSweep:
+    """Backward sweep of a stack of attention layers whose KV pools live in a
+    host tier ("Out of the Memory Barrier", gist.science de, section 2.C: the
+    next layer's KV is fetched while the current layer computes; the KV
+    gradients travel the same way; section 2.D: with page top-K only the
+    selected pages move).
+
+    For each chunk (last to first) and each layer (last to first): the
+    layer's selection is computed on the compute stream one layer ahead, its
+    pages (and their gradients) are prefetched on the copy stream while the
+    current layer's forward + backward run, and each layer's gradient pages
+    are written back on a third stream after its backward.  Only events
+    order the streams; the host never waits on the device inside the
+    sweep.
+
+    inputs(layer, chunk) -> dict(q_pos0, q, do) of device tensors.
+    """
+
+    def __init__(self, pool: Pool, n_layers: int, hq: int, hkv: int, d: int, page: int,
+                 scale: float, sparse: Optional[Sparse], dtype: torch.dtype,
+                 compute_stream=None, copy_stream=None, writeback_stream=None):
+        self.pool, self.L, self.hq, self.hkv, self.d, self.page = pool, n_layers, hq, hkv, d, page
+        self.scale, self.sparse, self.dtype = scale, sparse, dtype
+        self.compute = compute_stream or torch.cuda.current_stream()
+        # host -> HBM fetches and HBM -> host writebacks on separate streams so
+        # that both directions of the host link are busy at once
+        self.copy = copy_stream or torch.cuda.Stream()
+        self.wb = writeback_stream or torch.cuda.Stream()
+        self.sel = {}
+
+    def _select(self, layer: int, ch: dict, buf: ChunkBuffers):
+        if self.sparse is None:
+            return None
+        sel = buf.sel
+        pkv_select_topk_pages(self.pool, layer, ch["q_pos0"], ch["q"], self.sparse.top_k,
+                              sel[0], sel[1], self.sparse.n_sink, self.sparse.n_local,
+                              stream=self.compute)
+        return sel
+
+    def chunk(self, c: int, inputs, bufs, outputs=None):
+        """Backward-sweep step of chunk c over every layer.  bufs[layer]:
+        ChunkBuffers sized for this chunk (two alternating sets suffice).
+        outputs(layer, c, buf) is called after the layer's backward is
+        enqueued (on the compute stream) to collect results."""
+        from . import pkv_prefetch_pages, pkv_writeback_grads
+        L = self.L
+        ins = {L - 1: inputs(L - 1, c)}
+        sel = self._select(L - 1, ins[L - 1], bufs[L - 1])
+        ev = torch.cuda.Event()
+        ev.record(self.compute)
+        self.copy.wait_event(ev)
+        pkv_prefetch_pages(self.pool, L - 1, sel, with_grads=True, copy_stream=self.copy)
+        for layer in range(L - 1, -1, -1):
+            if layer - 1 >= 0:
+                ins[layer - 1] = inputs(layer - 1, c)
+                nsel = self._select(layer - 1, ins[layer - 1], bufs[layer - 1])
+                ev = torch.cuda.Event()
+                ev.record(self.compute)
+                self.copy.wait_event(ev)
+                pkv_prefetch_pages(self.pool, layer - 1, nsel, with_grads=True,
+                                   copy_stream=self.copy)
+            ch, b = ins.pop(layer), bufs[layer]
+            pkv_attn_fwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, b.lse, self.scale,
+                         sel=b.sel, stream=self.compute)
+            pkv_attn_bwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, ch["do"], b.lse, b.dq,
+                         self.scale, sel=b.sel, stream=self.compute)
+            if outputs is not None:
+                outputs(layer, c, b)
+            pkv_writeback_grads(self.pool, layer, copy_stream=self.wb)

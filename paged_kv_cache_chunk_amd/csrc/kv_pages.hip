@@ -43,22 +43,32 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i, bool bf16) 
   return reinterpret_cast<const float*>(p)[i];
 }
 
-// Mean of the keys present in each page (fixed order: row 0 upward), fp32.
-// grid (n_pages, hkv), block d threads.
-__global__ void reps_kernel(const void* __restrict__ kpool, float* __restrict__ reps,
-                            const int32_t* __restrict__ table, int page, int slots,
-                            int max_logical, int d, bool bf16, int64_t first_page,
-                            int64_t length) {
+// Mean of the keys present in each page, fp32.  grid (n_pages, hkv), block
+// 8 x d threads: part p sums rows p, p + 8, .. of its column, then the 8
+// partial sums are added in part order (fixed order).
+__global__ void __launch_bounds__(1024) reps_kernel(const void* __restrict__ kpool,
+                                                    float* __restrict__ reps,
+                                                    const int32_t* __restrict__ table, int page,
+                                                    int slots, int max_logical, int d, bool bf16,
+                                                    int64_t first_page, int64_t length) {
+  __shared__ float red[8][128];
   const int64_t j = first_page + blockIdx.x;
   const int g = blockIdx.y;
-  const int e = threadIdx.x;
+  const int e = threadIdx.x % d, part = threadIdx.x / d;
   const int slot = table[(int64_t)g * max_logical + j];
   int64_t n = length - j * page;
   if (n > page) n = page;
   const int64_t base = (((int64_t)g * slots + slot) * page) * d + e;
   float acc = 0.f;
-  for (int r = 0; r < n; ++r) acc += load_elem(kpool, base + (int64_t)r * d, bf16);
-  reps[((int64_t)g * slots + slot) * d + e] = acc / (float)n;
+  for (int r = part; r < n; r += 8) acc += load_elem(kpool, base + (int64_t)r * d, bf16);
+  red[part][e] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) sum += red[x][e];
+    reps[((int64_t)g * slots + slot) * d + e] = sum / (float)n;
+  }
 }
 
 // Logical-order export of K / V / dK / dV: dst[t][g][:] = pool[g][slot][t % P][:].
@@ -131,7 +141,7 @@ hipError_t launch_reps(const LayerDev& L, const Geom& g, bool bf16, int64_t firs
                        int64_t n_pages, int64_t length, hipStream_t s) {
   if (n_pages <= 0) return hipSuccess;
   KernelTimer t(KT_APPEND, s);
-  hipLaunchKernelGGL(reps_kernel, dim3((unsigned)n_pages, g.hkv), dim3(g.d), 0, s,
+  hipLaunchKernelGGL(reps_kernel, dim3((unsigned)n_pages, g.hkv), dim3(8 * g.d), 0, s,
                      (const void*)L.k, L.reps, L.table, g.page, g.slots, g.max_logical, g.d,
                      bf16, first_page, length);
   return hipGetLastError();

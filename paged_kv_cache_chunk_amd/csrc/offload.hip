@@ -8,7 +8,8 @@
 // move).  The union of the pages a selection names is marked in a per-window
 // byte map; one workgroup per (page, KV head) then copies that page-head if
 // marked.  Gradients travel as the host gradient dtype and live in HBM as
-// fp32 while the layer computes.
+// fp32 while the layer computes.  Two device counters add up the bytes
+// fetched and written back.
 #include "pkv_pool.h"
 
 namespace pkv {
@@ -39,78 +40,122 @@ __global__ void need_mark_all_kernel(uint8_t* need, int max_logical, int64_t n_p
   if (j < n_pages) need[(int64_t)blockIdx.y * max_logical + j] = 1;
 }
 
+// Copies `bytes` (a multiple of 4 KiB) with every thread keeping 4 16-byte
+// loads in flight (host-mapped sources are slow to answer).
 __device__ __forceinline__ void copy_bytes(char* __restrict__ dst, const char* __restrict__ src,
                                            int64_t bytes) {
-  for (int64_t i = threadIdx.x * 16; i < bytes; i += (int64_t)blockDim.x * 16)
-    *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+  const int64_t step = (int64_t)blockDim.x * 16;
+  for (int64_t i = threadIdx.x * 16; i < bytes; i += 4 * step) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * step < bytes) v[u] = *reinterpret_cast<const uint4*>(src + i + u * step);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * step < bytes) *reinterpret_cast<uint4*>(dst + i + u * step) = v[u];
+  }
 }
 
-// grid (n_pages, hkv), block 256.  One page-head per workgroup.
+__device__ __forceinline__ float4 lo4(uint4 a) {
+  return make_float4(__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xffff0000u),
+                     __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 hi4(uint4 a) {
+  return make_float4(__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xffff0000u),
+                     __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xffff0000u));
+}
+
+// bf16 [n] -> fp32 [n], n a multiple of 8 * blockDim * 2.
+__device__ __forceinline__ void widen(float* __restrict__ dst, const unsigned short* __restrict__ src,
+                                      int64_t n) {
+  const int64_t n8 = n / 8;
+  for (int64_t i = threadIdx.x; i < n8; i += 2 * (int64_t)blockDim.x) {
+    const uint4 a = reinterpret_cast<const uint4*>(src)[i];
+    const bool two = i + blockDim.x < n8;
+    uint4 b = a;
+    if (two) b = reinterpret_cast<const uint4*>(src)[i + blockDim.x];
+    float4* d = reinterpret_cast<float4*>(dst + 8 * i);
+    d[0] = lo4(a);
+    d[1] = hi4(a);
+    if (two) {
+      float4* e = reinterpret_cast<float4*>(dst + 8 * (i + blockDim.x));
+      e[0] = lo4(b);
+      e[1] = hi4(b);
+    }
+  }
+}
+
+// Work items are (page, KV head) pairs; a small persistent grid (kCopyBlocks
+// workgroups) walks them so that the copies occupy a few CUs next to the
+// attention kernels instead of flooding the whole GPU.
+constexpr int kCopyBlocks = 24;
+
 __global__ void __launch_bounds__(256) fetch_kernel(
     const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
-    int slots, int64_t page_elems, int kv_bytes, const char* __restrict__ hk,
-    const char* __restrict__ hv, char* __restrict__ wk, char* __restrict__ wv, bool with_grads,
-    bool grad_bf16, const void* __restrict__ hdk, const void* __restrict__ hdv,
-    float* __restrict__ wdk, float* __restrict__ wdv) {
-  const int j = blockIdx.x, g = blockIdx.y;
-  if (!need[(int64_t)g * max_logical + j]) return;
-  const int slot = table[(int64_t)g * max_logical + j];
-  const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
-  copy_bytes(wk + e0 * kv_bytes, hk + e0 * kv_bytes, page_elems * kv_bytes);
-  copy_bytes(wv + e0 * kv_bytes, hv + e0 * kv_bytes, page_elems * kv_bytes);
-  if (!with_grads) return;
-  if (!grad_bf16) {
-    copy_bytes((char*)(wdk + e0), (const char*)hdk + e0 * 4, page_elems * 4);
-    copy_bytes((char*)(wdv + e0), (const char*)hdv + e0 * 4, page_elems * 4);
-    return;
+    int slots, int hkv, int n_pages, int64_t page_elems, int kv_bytes,
+    const char* __restrict__ hk, const char* __restrict__ hv, char* __restrict__ wk,
+    char* __restrict__ wv, bool with_grads, bool grad_bf16, const void* __restrict__ hdk,
+    const void* __restrict__ hdv, float* __restrict__ wdk, float* __restrict__ wdv,
+    unsigned long long* __restrict__ moved) {
+  unsigned long long mine = 0;
+  for (int item = blockIdx.x; item < n_pages * hkv; item += gridDim.x) {
+    const int g = item % hkv, j = item / hkv;
+    if (!need[(int64_t)g * max_logical + j]) continue;
+    const int slot = table[(int64_t)g * max_logical + j];
+    const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
+    copy_bytes(wk + e0 * kv_bytes, hk + e0 * kv_bytes, page_elems * kv_bytes);
+    copy_bytes(wv + e0 * kv_bytes, hv + e0 * kv_bytes, page_elems * kv_bytes);
+    mine += 2 * page_elems * kv_bytes;
+    if (!with_grads) continue;
+    if (!grad_bf16) {
+      copy_bytes((char*)(wdk + e0), (const char*)hdk + e0 * 4, page_elems * 4);
+      copy_bytes((char*)(wdv + e0), (const char*)hdv + e0 * 4, page_elems * 4);
+      mine += 2 * page_elems * 4;
+    } else {
+      widen(wdk + e0, (const unsigned short*)hdk + e0, page_elems);
+      widen(wdv + e0, (const unsigned short*)hdv + e0, page_elems);
+      mine += 2 * page_elems * 2;
+    }
   }
-  const uint4* sk = reinterpret_cast<const uint4*>((const unsigned short*)hdk + e0);
-  const uint4* sv = reinterpret_cast<const uint4*>((const unsigned short*)hdv + e0);
-  for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
-    const uint4 a = sk[i], b = sv[i];
-    const unsigned ua[4] = {a.x, a.y, a.z, a.w}, ub[4] = {b.x, b.y, b.z, b.w};
-    float4* dk4 = reinterpret_cast<float4*>(wdk + e0 + 8 * i);
-    float4* dv4 = reinterpret_cast<float4*>(wdv + e0 + 8 * i);
-    dk4[0] = make_float4(__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
-                         __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u));
-    dk4[1] = make_float4(__uint_as_float(ua[2] << 16), __uint_as_float(ua[2] & 0xffff0000u),
-                         __uint_as_float(ua[3] << 16), __uint_as_float(ua[3] & 0xffff0000u));
-    dv4[0] = make_float4(__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
-                         __uint_as_float(ub[1] << 16), __uint_as_float(ub[1] & 0xffff0000u));
-    dv4[1] = make_float4(__uint_as_float(ub[2] << 16), __uint_as_float(ub[2] & 0xffff0000u),
-                         __uint_as_float(ub[3] << 16), __uint_as_float(ub[3] & 0xffff0000u));
-  }
+  if (threadIdx.x == 0 && mine) atomicAdd(moved, mine);
 }
 
 __device__ __forceinline__ unsigned to_bf16(float x) {
   return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
-// grid (n_pages, hkv), block 256: window fp32 grads -> host gradient dtype.
+// window fp32 grads -> host gradient dtype, same persistent walk.
 __global__ void __launch_bounds__(256) writeback_kernel(
     const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
-    int slots, int64_t page_elems, bool grad_bf16, void* __restrict__ hdk,
-    void* __restrict__ hdv, const float* __restrict__ wdk, const float* __restrict__ wdv) {
-  const int j = blockIdx.x, g = blockIdx.y;
-  if (!need[(int64_t)g * max_logical + j]) return;
-  const int slot = table[(int64_t)g * max_logical + j];
-  const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
-  if (!grad_bf16) {
-    copy_bytes((char*)hdk + e0 * 4, (const char*)(wdk + e0), page_elems * 4);
-    copy_bytes((char*)hdv + e0 * 4, (const char*)(wdv + e0), page_elems * 4);
-    return;
+    int slots, int hkv, int n_pages, int64_t page_elems, bool grad_bf16, void* __restrict__ hdk,
+    void* __restrict__ hdv, const float* __restrict__ wdk, const float* __restrict__ wdv,
+    unsigned long long* __restrict__ moved) {
+  unsigned long long mine = 0;
+  for (int item = blockIdx.x; item < n_pages * hkv; item += gridDim.x) {
+    const int g = item % hkv, j = item / hkv;
+    if (!need[(int64_t)g * max_logical + j]) continue;
+    const int slot = table[(int64_t)g * max_logical + j];
+    const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
+    if (!grad_bf16) {
+      copy_bytes((char*)hdk + e0 * 4, (const char*)(wdk + e0), page_elems * 4);
+      copy_bytes((char*)hdv + e0 * 4, (const char*)(wdv + e0), page_elems * 4);
+      mine += 2 * page_elems * 4;
+      continue;
+    }
+    uint4* dk = reinterpret_cast<uint4*>((unsigned short*)hdk + e0);
+    uint4* dv = reinterpret_cast<uint4*>((unsigned short*)hdv + e0);
+    for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
+      const float4* a = reinterpret_cast<const float4*>(wdk + e0 + 8 * i);
+      const float4* b = reinterpret_cast<const float4*>(wdv + e0 + 8 * i);
+      const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+      dk[i] = make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
+                         to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
+      dv[i] = make_uint4(to_bf16(b0.x) | (to_bf16(b0.y) << 16), to_bf16(b0.z) | (to_bf16(b0.w) << 16),
+                         to_bf16(b1.x) | (to_bf16(b1.y) << 16), to_bf16(b1.z) | (to_bf16(b1.w) << 16));
+    }
+    mine += 2 * page_elems * 2;
   }
-  uint4* dk = reinterpret_cast<uint4*>((unsigned short*)hdk + e0);
-  uint4* dv = reinterpret_cast<uint4*>((unsigned short*)hdv + e0);
-  for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
-    const float4* a = reinterpret_cast<const float4*>(wdk + e0 + 8 * i);
-    const float4* b = reinterpret_cast<const float4*>(wdv + e0 + 8 * i);
-    const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-    dk[i] = make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
-                       to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
-    dv[i] = make_uint4(to_bf16(b0.x) | (to_bf16(b0.y) << 16), to_bf16(b0.z) | (to_bf16(b0.w) << 16),
-                       to_bf16(b1.x) | (to_bf16(b1.y) << 16), to_bf16(b1.z) | (to_bf16(b1.w) << 16));
-  }
+  if (threadIdx.x == 0 && mine) atomicAdd(moved, mine);
 }
 
 // dst[t][g][:] (fp32) = bf16 host gradient of token t
@@ -167,14 +212,15 @@ hipError_t launch_fetch_pages(const pkv_pool* p, int layer, int window, bool wit
   const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
   const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
   KernelTimer t(KT_FETCH, s);
-  hipLaunchKernelGGL(fetch_kernel, dim3((unsigned)n_pages, d.n_kv_heads), dim3(256), 0, s, need,
-                     table, d.max_logical_pages, d.n_slots, page_elems, p->kv_bytes,
+  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, need,
+                     table, d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)n_pages, page_elems,
+                     p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
                      (char*)p->d_k + window * p->layer_elems * p->kv_bytes,
                      (char*)p->d_v + window * p->layer_elems * p->kv_bytes, with_grads,
                      d.host_grad_dtype == PKV_BF16, (const void*)p->m_dk[layer],
                      (const void*)p->m_dv[layer], p->d_dk + window * p->layer_elems,
-                     p->d_dv + window * p->layer_elems);
+                     p->d_dv + window * p->layer_elems, p->d_moved);
   return hipGetLastError();
 }
 
@@ -186,11 +232,11 @@ hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipS
   const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
   const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
   KernelTimer t(KT_WRITEBACK, s);
-  hipLaunchKernelGGL(writeback_kernel, dim3((unsigned)n_pages, d.n_kv_heads), dim3(256), 0, s,
-                     need, table, d.max_logical_pages, d.n_slots, page_elems,
-                     d.host_grad_dtype == PKV_BF16, p->m_dk[layer], p->m_dv[layer],
+  hipLaunchKernelGGL(writeback_kernel, dim3(kCopyBlocks), dim3(256), 0, s,
+                     need, table, d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)n_pages,
+                     page_elems, d.host_grad_dtype == PKV_BF16, p->m_dk[layer], p->m_dv[layer],
                      (const float*)(p->d_dk + window * p->layer_elems),
-                     (const float*)(p->d_dv + window * p->layer_elems));
+                     (const float*)(p->d_dv + window * p->layer_elems), p->d_moved + 1);
   return hipGetLastError();
 }
 

@@ -375,6 +375,11 @@ pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
   return pool_prefetch(pool, layer, sel, with_grads != 0, copy_stream, ready);
 }
 
+pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written) {
+  if (!pool) return fail(PKV_EINVAL, "pkv_offload_bytes: null pool");
+  return pool_copy_stats(pool, fetched, written);
+}
+
 pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_stream,
                                hipEvent_t done) {
   if (!pool) return fail(PKV_EINVAL, "pkv_writeback_grads: null pool");

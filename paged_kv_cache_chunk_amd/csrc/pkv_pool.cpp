@@ -58,7 +58,7 @@ pkv_status pool_allocate(pkv_pool* p) {
   const int64_t tabb = (int64_t)d.n_layers * d.n_kv_heads * d.max_logical_pages * 4;
   const int64_t needb = d.host_tier ? (int64_t)pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
   if (d.host_tier && d.device_budget_bytes > 0 &&
-      2 * kvb + 2 * grb + repb + tabb + needb > d.device_budget_bytes)
+      2 * kvb + 2 * grb + repb + tabb + needb + 16 > d.device_budget_bytes)
     return pool_fail(PKV_ENOMEM, "host-tier window does not fit device_budget_bytes");
   if ((st = dev_alloc(p, &p->d_k, kvb, "device allocation of the K pool failed")) != PKV_OK) return st;
   if ((st = dev_alloc(p, &p->d_v, kvb, "device allocation of the V pool failed")) != PKV_OK) return st;
@@ -70,6 +70,7 @@ pkv_status pool_allocate(pkv_pool* p) {
   if (e != hipSuccess) return pool_hip_fail(e, "hipMemcpy (page tables)");
   if (d.host_tier) {
     if ((st = dev_alloc(p, (void**)&p->d_need, needb, "device allocation of the window map failed")) != PKV_OK) return st;
+    if ((st = dev_alloc(p, (void**)&p->d_moved, 16, "device allocation of the copy counters failed")) != PKV_OK) return st;
     for (int w = 0; w < pkv_pool::kWindow; ++w) {
       if ((e = hipEventCreateWithFlags(&p->ev_compute[w], hipEventDisableTiming)) != hipSuccess)
         return pool_hip_fail(e, "hipEventCreate");
@@ -112,7 +113,7 @@ pkv_status pool_release(pkv_pool* p) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) st = pool_hip_fail(e, "hipDeviceSynchronize (pool destroy)");
   void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_delta,
-                 p->d_select, p->d_need};
+                 p->d_select, p->d_need, p->d_moved};
   for (void* x : dev)
     if (x) (void)hipFree(x);
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
@@ -261,6 +262,23 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
   p->wb_recorded[w] = true;
   if (done && (e = hipEventRecord(done, cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (writeback done)");
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+namespace pkv {
+
+pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written) {
+  unsigned long long h[2] = {0, 0};
+  if (p->d_moved) {
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return pool_hip_fail(e, "pkv_offload_bytes: sync");
+    e = hipMemcpy(h, p->d_moved, sizeof h, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return pool_hip_fail(e, "pkv_offload_bytes: copy");
+  }
+  if (fetched) *fetched = (int64_t)h[0];
+  if (written) *written = (int64_t)h[1];
   return PKV_OK;
 }
 

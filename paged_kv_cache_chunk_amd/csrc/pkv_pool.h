@@ -45,6 +45,7 @@ struct pkv_pool {
   bool compute_recorded[kWindow] = {false, false};
   bool ready_recorded[kWindow] = {false, false};
   uint8_t* d_need = nullptr;      // [kWindow][Hkv][max_logical] pages held by the window
+  unsigned long long* d_moved = nullptr;  // [0] bytes fetched, [1] bytes written back
 
   int window_of(int layer) const { return layer % kWindow; }
 };
@@ -68,6 +69,7 @@ pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_grads,
                          hipStream_t copy_stream, hipEvent_t ready);
 pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t copy_stream, hipEvent_t done);
+pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written);
 
 // offload.hip
 hipError_t launch_need_clear(uint8_t* need, int64_t n, hipStream_t s);

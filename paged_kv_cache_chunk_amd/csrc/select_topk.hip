@@ -27,18 +27,58 @@ __device__ __forceinline__ float ld(const void* p, int64_t i, bool bf16) {
   return reinterpret_cast<const float*>(p)[i];
 }
 
-// grid (n_qpages, hkv), block d.  Fixed summation order: token-major, then head.
-__global__ void qmean_kernel(const void* __restrict__ q, float* __restrict__ qbar, int hq,
-                             int hkv, int d, int page, int n_q, bool bf16) {
-  const int il = blockIdx.x, g = blockIdx.y, e = threadIdx.x;
+// grid (n_qpages, hkv), block 1024.  Thread (part p = tid / 32, lane j =
+// tid % 32) sums columns j*E .. j*E+E-1 (E = d / 32) over the (token, head)
+// pairs p, p + 32, .. of the page's group in that order; the 32 partial
+// sums are then added in part order.  Fixed order, so reruns are
+// bit-identical.
+template <int DD>
+__global__ void __launch_bounds__(1024) qmean_kernel(const void* __restrict__ q,
+                                                     float* __restrict__ qbar, int hq, int hkv,
+                                                     int page, int n_q, bool bf16) {
+  constexpr int E = DD / 32;
+  constexpr int NP = 32;
+  __shared__ float red[NP][DD];
+  const int il = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int part = tid >> 5, j = tid & 31;
   const int G = hq / hkv;
   const int t0 = il * page;
   int t1 = t0 + page;
   if (t1 > n_q) t1 = n_q;
-  float acc = 0.f;
-  for (int t = t0; t < t1; ++t)
-    for (int h = g * G; h < (g + 1) * G; ++h) acc += ld(q, ((int64_t)t * hq + h) * d + e, bf16);
-  qbar[((int64_t)il * hkv + g) * d + e] = acc / (float)((t1 - t0) * G);
+  const int n_pairs = (t1 - t0) * G;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int pr = part; pr < n_pairs; pr += NP) {
+    const int t = t0 + pr / G, h = g * G + pr % G;
+    const int64_t base = ((int64_t)t * hq + h) * DD + j * E;
+    if (bf16) {
+      // E consecutive bf16 values (4 or 2): one 8- or 4-byte load
+      const unsigned short* p = reinterpret_cast<const unsigned short*>(q) + base;
+      if (E == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        acc[0] += __uint_as_float(v.x << 16);
+        acc[1] += __uint_as_float(v.x & 0xffff0000u);
+        acc[E > 2 ? 2 : 0] += E > 2 ? __uint_as_float(v.y << 16) : 0.f;
+        acc[E > 3 ? 3 : 0] += E > 3 ? __uint_as_float(v.y & 0xffff0000u) : 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += __uint_as_float(((unsigned)p[e]) << 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += reinterpret_cast<const float*>(q)[base + e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[part][j * E + e] = acc[e];
+  __syncthreads();
+  if (tid < DD) {
+    float sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < NP; ++x) sum += red[x][tid];
+    qbar[((int64_t)il * hkv + g) * DD + tid] = sum / (float)n_pairs;
+  }
 }
 
 // grid (n_qpages, hkv, ceil(max_cand / 256)), block 256.  Sequential fma over d.
@@ -75,6 +115,23 @@ __device__ __forceinline__ unsigned fkey(float x) {
 }
 
 constexpr int kTB = 256;  // threads per selection workgroup
+
+// Inclusive prefix sum of x across the workgroup in thread order (wavefront
+// shuffles, then the 4 wave totals through LDS).
+__device__ int block_incl_scan(int x, int* wave_tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[w] = x;
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < w; ++v) before += wave_tot[v];
+  __syncthreads();
+  return x + before;
+}
 
 // Exclusive prefix of `flag` across the workgroup in thread order; returns the
 // prefix and writes the workgroup total to *total.  Uses wavefront ballots.
@@ -132,14 +189,16 @@ __global__ void __launch_bounds__(kTB) topk_kernel(const float* __restrict__ sco
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, b = 255;
-        for (; b > 0; --b) {
-          if (cum + (int)hist[b] >= k) break;
-          cum += (int)hist[b];
+      // suffix sums over the bins: S(b) = count of digits >= b; the digit of
+      // the k-th largest is the b with S(b) >= k > S(b + 1)
+      {
+        const int b = 255 - tid;  // tid < 256 == kTB
+        const int above = block_incl_scan((int)hist[b], wave_tot) - (int)hist[b];  // S(b + 1)
+        const int at = above + (int)hist[b];                                          // S(b)
+        if (at >= k && above < k) {
+          s_digit = b;
+          s_k = k - above;
         }
-        s_digit = b;
-        s_k = k - cum;
       }
       __syncthreads();
       prefix |= ((unsigned)s_digit) << shift;
@@ -202,8 +261,12 @@ hipError_t launch_select(const LayerDev& L, const Geom& g, bool bf16, int hq, in
   KernelTimer t(KT_SELECT, s);
   float* qbar = scratch;
   float* scores = scratch + (int64_t)nqp * g.hkv * g.d;
-  hipLaunchKernelGGL(qmean_kernel, dim3(nqp, g.hkv), dim3(g.d), 0, s, q, qbar, hq, g.hkv, g.d,
-                     g.page, n_q, bf16);
+  if (g.d == 64)
+    hipLaunchKernelGGL(qmean_kernel<64>, dim3(nqp, g.hkv), dim3(1024), 0, s, q, qbar, hq, g.hkv,
+                       g.page, n_q, bf16);
+  else
+    hipLaunchKernelGGL(qmean_kernel<128>, dim3(nqp, g.hkv), dim3(1024), 0, s, q, qbar, hq, g.hkv,
+                       g.page, n_q, bf16);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(score_kernel, dim3(nqp, g.hkv, (max_cand + 255) / 256), dim3(256), 0, s,

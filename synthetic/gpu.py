@@ -53,16 +53,33 @@ class GpuWorkload:
         x1, x2 = x[..., :half], x[..., half:]
         return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
 
-    def chunk(self, c: int) -> dict:
-        """{'q_pos0', 'q', 'k', 'v', 'do'} as device tensors in the storage dtype."""
+    def chunk(self, c: int, parts: str = "qkvd") -> dict:
+        """{'q_pos0', 'q', 'k', 'v', 'do'} as device tensors in the storage
+        dtype; `parts` limits which tensors are drawn (each has its own
+        substream, so a subset gives the same values)."""
         cfg = self.cfg
         pos0, n = cfg.chunk_range(c)
-        q = self._draw(c, _Q, (n, cfg.hq, cfg.d))
+        out = dict(q_pos0=pos0)
+        dt = self.dtype
+        if "q" in parts:
+            q = self._draw(c, _Q, (n, cfg.hq, cfg.d))
+            if cfg.rope_base:
+                q = self._rope(q, pos0)
+            out["q"] = q.to(dt).contiguous()
+        if "d" in parts:
+            do = self._draw(c, _DO, (n, cfg.hq, cfg.d))
+            if cfg.do_scale != 1.0:
+                do *= cfg.do_scale
+            out["do"] = do.to(dt).contiguous()
+        if "v" in parts:
+            out["v"] = self._draw(c, _V, (n, cfg.hkv, cfg.d)).to(dt).contiguous()
+        if "k" in parts:
+            out["k"] = self._keys(c, pos0, n).to(dt).contiguous()
+        return out
+
+    def _keys(self, c: int, pos0: int, n: int) -> torch.Tensor:
+        cfg = self.cfg
         k = self._draw(c, _K, (n, cfg.hkv, cfg.d))
-        v = self._draw(c, _V, (n, cfg.hkv, cfg.d))
-        do = self._draw(c, _DO, (n, cfg.hq, cfg.d))
-        if cfg.do_scale != 1.0:
-            do *= cfg.do_scale
         if cfg.planted_frac > 0:
             for g, (pages, u) in self.cpu.planted().items():
                 lo_p, hi_p = pos0 // cfg.page, (pos0 + n - 1) // cfg.page
@@ -72,8 +89,5 @@ class GpuWorkload:
                     hi = min((int(p) + 1) * cfg.page, pos0 + n)
                     k[lo - pos0:hi - pos0, g, :] += torch.from_numpy(off.astype(np.float32)).to(self.device)
         if cfg.rope_base:
-            q = self._rope(q, pos0)
             k = self._rope(k, pos0)
-        dt = self.dtype
-        return dict(q_pos0=pos0, q=q.to(dt).contiguous(), k=k.to(dt).contiguous(),
-                    v=v.to(dt).contiguous(), do=do.to(dt).contiguous())
+        return k
