@@ -19,6 +19,7 @@ Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
@@ -38,9 +39,13 @@ def log(*a):
 
 
 def source_hash() -> str:
+    """Hash of the bf16 attention kernel sources and their compile flags: stored
+    counter readings only apply to the kernels they were taken on."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "paged_kv_cache_chunk_amd", "csrc", "attn_bf16.hip"), "rb") as f:
-        h.update(f.read())
+    pkg = os.path.join(ROOT, "paged_kv_cache_chunk_amd")
+    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "attn_bf16_*"))) + [os.path.join(pkg, "build.py")]:
+        with open(p, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

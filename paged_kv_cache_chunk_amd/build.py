@@ -29,6 +29,17 @@ COMMON = [
 ]
 
 
+# Per-source machine-scheduler strategy of the LLVM AMDGPU backend, chosen by
+# measurement on MI355X: the dK/dV and forward kernels (one or two waves per
+# SIMD, register-bound) gain from the iterative ILP scheduler, which hoists LDS
+# reads ahead of the MFMAs that consume them; the dQ kernel from the max-ILP one.
+SOURCE_FLAGS = {
+    "attn_bf16_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bf16_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bf16_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -38,7 +49,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

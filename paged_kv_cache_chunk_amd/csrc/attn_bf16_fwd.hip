@@ -1,0 +1,206 @@
+// bf16 paged attention forward for gfx950 (tile layout, swizzle and operand
+// layouts are described in attn_bf16_tiles.h).
+//
+// Per query chunk and head, the online-softmax forward of exact causal
+// attention over the paged keys ("Out of the Memory Barrier", gist.science
+// de, sections 2.A and 2.B): O and the log-sum-exp of every row.
+#include "attn_bf16_tiles.h"
+
+namespace pkv {
+namespace {
+
+// NT: 32-row column tiles per wave (a wave owns 32*NT query rows);
+// BNT: keys per tile.  A workgroup owns 128 rows of one query head.
+template <int NT, int BNT>
+__global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_bf16_kernel(AttnCall c, int n_qblocks) {
+  constexpr int NW = 4 / NT;          // waves per workgroup
+  constexpr int MT = BNT / 32;        // 32-key m-tiles per tile
+  constexpr int TB = BNT * ROWB;      // bytes per K or V tile
+  __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
+  const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  // Workgroup -> (query block, head): workgroups are dealt to the 8 XCDs
+  // round-robin, so bid % Hkv = KV head keeps every head's workgroups on the
+  // same XCDs (sharing their L2 for that head's K/V); longest rows first.
+  const int G = c.hq / c.g.hkv;
+  const int bid = blockIdx.x;
+  const int g = uni(bid % c.g.hkv), m = uni(bid / c.g.hkv);
+  const int qb = n_qblocks - 1 - m / G;
+  const int h = g * G + m % G;
+  const int r0 = qb * BM;
+  const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
+  const int rw0 = r0 + 32 * NT * w;   // wave's first row (relative to q_pos0)
+  const int tw_min = rw0 < rlast ? rw0 : rlast;
+  const int tw_max = rw0 + 32 * NT - 1 < rlast ? rw0 + 32 * NT - 1 : rlast;
+
+  bf16x8 qf[NT][8];
+  int t_rel[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    int r = rw0 + 32 * nt + l32;
+    r = r < rlast ? r : rlast;
+    t_rel[nt] = r;
+    const u16* qrow = reinterpret_cast<const u16*>(c.q) + ((int64_t)r * c.hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[nt][ks] = as_bf16x8(ld16(qrow + 16 * ks));
+  }
+
+  int n_tiles;
+  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, rlast, &n_tiles);
+  TileDma<BNT, NW> dma;
+  dma.init(w, lane);
+  auto issue = [&](int b, const KeyTile& t) {
+    dma.issue(sm[b], w, key_rows<BNT>(c, c.L.k, g, t), ROWB);
+    dma.issue(sm[b] + TB, w, key_rows<BNT>(c, c.L.v, g, t), ROWB);
+  };
+
+  f32x16 oacc[4][NT];
+  float m_ref[NT], l_i[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt][nt] = f32x16{};
+    m_ref[nt] = -INFINITY;
+    l_i[nt] = 0.f;
+  }
+  const float c2 = c.scale * kLog2e;
+
+  KeyTile t_cur{0, 0, 0};
+  if (n_tiles > 0) {
+    t_cur = walk.next();
+    issue(0, t_cur);
+  }
+  wait_dma_and_sync();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int b = j & 1;
+    KeyTile t_next{0, 0, 0};
+    if (j + 1 < n_tiles) {
+      t_next = walk.next();
+      issue(b ^ 1, t_next);
+    }
+    const char* kt = sm[b];
+    const char* vt = sm[b] + TB;
+    const int srel0 = t_cur.srel0;  // tile's first key, relative to q_pos0
+    if (srel0 <= tw_max) {
+      f32x16 sacc[MT][NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 a = frag_row(kt, 32 * mt + l32, ks, half);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma(a, qf[nt][ks], sacc[mt][nt]);
+        }
+      }
+      if (srel0 + BNT - 1 > tw_min) {  // tile crosses the causal diagonal of this wave
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int sr = srel0 + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (sr > t_rel[nt]) sacc[mt][nt][r] = -INFINITY;
+            }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+        // Lazy rescale: keep the reference maximum unless a row's maximum
+        // grew by more than 2^8 (probabilities stay <= 256, exact enough in
+        // fp32 and representable in bf16).
+        if (__any(mx > m_ref[nt] + 8.f)) {
+          const float mr = fmaxf(m_ref[nt], mx);
+          const float alpha = ex2(m_ref[nt] - mr);
+          l_i[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt][nt] *= alpha;
+          m_ref[nt] = mr;
+        }
+        const float mneg = -m_ref[nt];
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = ex2(fmaf(sacc[mt][nt][r], c2, mneg));
+            sacc[mt][nt][r] = p;
+            rs += p;
+          }
+        l_i[nt] += rs;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2 * MT; ++kk) {
+        bf16x8 pf[NT];
+        const int mt = kk >> 1, rb = 8 * (kk & 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          u32x4 pv;
+          pv.x = pack2(sacc[mt][nt][rb + 0], sacc[mt][nt][rb + 1]);
+          pv.y = pack2(sacc[mt][nt][rb + 2], sacc[mt][nt][rb + 3]);
+          pv.z = pack2(sacc[mt][nt][rb + 4], sacc[mt][nt][rb + 5]);
+          pv.w = pack2(sacc[mt][nt][rb + 6], sacc[mt][nt][rb + 7]);
+          pf[nt] = as_bf16x8(pv);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 a = frag_tr(vt, 16 * kk, 32 * dt, lane);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma(a, pf[nt], oacc[dt][nt]);
+        }
+      }
+    }
+    t_cur = t_next;
+    wait_dma_and_sync();
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int my_r = rw0 + 32 * nt + l32;
+    const float lt = l_i[nt] + __shfl_xor(l_i[nt], 32);
+    if (my_r <= rlast) {
+      const float inv = 1.f / lt;
+      u16* orow = reinterpret_cast<u16*>(c.o_out) + ((int64_t)my_r * c.hq + h) * D + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          u32x2 v;
+          v.x = pack2(oacc[dt][nt][4 * j4 + 0] * inv, oacc[dt][nt][4 * j4 + 1] * inv);
+          v.y = pack2(oacc[dt][nt][4 * j4 + 2] * inv, oacc[dt][nt][4 * j4 + 3] * inv);
+          st8(orow + 32 * dt + 8 * j4, v);
+        }
+      }
+      if (half == 0) c.lse[(int64_t)h * c.n_q + my_r] = (m_ref[nt] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s) {
+  const int nqb = (c.n_q + BM - 1) / BM;
+  static const int choice = tile_choice("PKV_FWD_TILE", 0);
+  KernelTimer t(KT_FWD, s);
+  switch (choice) {
+    case 1:
+      hipLaunchKernelGGL((fwd_bf16_kernel<2, 32>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
+      break;
+    case 2:
+      hipLaunchKernelGGL((fwd_bf16_kernel<2, 64>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
+      break;
+    default:
+      hipLaunchKernelGGL((fwd_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -93,9 +93,10 @@ int64_t select_scratch_floats(const Geom& g, int64_t q_pos0, int n_q, int n_sink
 hipError_t launch_fwd_f32(const AttnCall& c, hipStream_t s);
 hipError_t launch_bwd_f32(const AttnCall& c, hipStream_t s);
 
-// ---- kernels in attn_bf16.hip
+// ---- kernels in attn_bf16_fwd.hip, attn_bf16_dq.hip, attn_bf16_dkdv.hip
 hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s);
-hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s);
+hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s);  // D, lse2, dQ, dK/dV
+hipError_t launch_dq_bf16(const AttnCall& c, hipStream_t s);   // dQ only (D, lse2 written)
 
 // ---- kernels in attn_common.hip
 hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s);
