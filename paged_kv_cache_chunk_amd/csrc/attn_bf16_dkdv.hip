@@ -17,11 +17,111 @@ struct __align__(1024) DkvSmem {
   char o[2][BQT * ROWB];
   float lsd[2][2 * BQT];  // per buffer: LSE of the BQT rows, then D of the BQT rows
   int qpl[1024];
-  int n_qpl;
 };
 
-// grid ceil(n_keys / 128) * hkv * splits.  BQT: query rows per tile (32 or
-// 64); OCC: waves per SIMD the register budget is sized for.
+// Work list of the sparse dK/dV kernel (layout in DkvPlan), one workgroup of
+// 1024 threads.  The selection is inverted: for every (KV head g, key page p)
+// the ascending list of the query pages whose selection holds p.  A key page
+// that many query pages selected (the sink pages, pages every query scores
+// high) would otherwise leave one workgroup with all their rows while the
+// rest of the grid idles; here its work is cut into items of at most qpi
+// query pages.  Item order: (g, p, 128-key slab of p, piece).
+__global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, int G, int page,
+                                                         int tiles_pp, DkvPlan pl) {
+  __shared__ int s_a[1024], s_b[1024];
+  const int tid = threadIdx.x;
+  int* cnt = pl.base + pl.off_cnt;
+  int* off = pl.base + pl.off_off;
+  int* lst = pl.base + pl.off_lst;
+  int4* items = reinterpret_cast<int4*>(pl.base + pl.off_items);
+  const int E = hkv * pl.n_pages;
+  const int subs = page / 128;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  // count (atomics keep the counts exact even if a list names a page twice)
+  const int per_qp = hkv * sel.stride;
+  for (int il = 0; il < sel.n_qpages; ++il) {
+    for (int x = tid; x < per_qp; x += 1024) {
+      const int g = x / sel.stride, j = x % sel.stride;
+      int n = sel.count[(int64_t)il * hkv + g];
+      n = n < 0 ? 0 : (n > sel.stride ? sel.stride : n);
+      if (j < n) {
+        const int p = sel.pages[((int64_t)il * hkv + g) * sel.stride + j];
+        if (p >= 0 && p < pl.n_pages) atomicAdd(&cnt[g * pl.n_pages + p], 1);
+      }
+    }
+    __syncthreads();
+  }
+  // exclusive scans of list lengths and item counts; thread t owns a
+  // contiguous run of entries
+  const int run = (E + 1023) / 1024;
+  const int e0 = tid * run < E ? tid * run : E;
+  const int e1 = e0 + run < E ? e0 + run : E;
+  auto n_items = [&](int c) { return c > 0 ? subs * ((c + pl.qpi - 1) / pl.qpi) : 0; };
+  // the counters were updated by atomics (at L2): read them past the L1
+  auto count_of = [&](int e) { return __hip_atomic_load(&cnt[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  int sa = 0, sb = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int cv = count_of(e);
+    sa += cv;
+    sb += n_items(cv);
+  }
+  s_a[tid] = sa;
+  s_b[tid] = sb;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int va = tid >= d ? s_a[tid - d] : 0;
+    const int vb = tid >= d ? s_b[tid - d] : 0;
+    __syncthreads();
+    s_a[tid] += va;
+    s_b[tid] += vb;
+    __syncthreads();
+  }
+  int oa = s_a[tid] - sa, ob = s_b[tid] - sb;
+  const int total_items = s_b[1023] < pl.max_items ? s_b[1023] : pl.max_items;
+  for (int e = e0; e < e1; ++e) {
+    const int cv = count_of(e);
+    off[e] = oa;
+    oa += cv;
+    if (cv == 0) continue;
+    const int g = e / pl.n_pages, p = e % pl.n_pages;
+    const int it_total = cv * tiles_pp * G;
+    const int it_step = pl.qpi * tiles_pp * G;
+    for (int sub = 0; sub < subs; ++sub)
+      for (int i0 = 0; i0 < it_total; i0 += it_step) {
+        const int i1 = i0 + it_step < it_total ? i0 + it_step : it_total;
+        if (ob < pl.max_items) items[ob] = make_int4(g, p * subs + sub, i0, i1);
+        ++ob;
+      }
+  }
+  if (tid == 0) pl.base[0] = total_items;
+  __syncthreads();  // every thread has read its counts before they are reset
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;  // reused as fill cursors
+  __syncthreads();
+  // fill one query page at a time, so every list is ascending; each entry
+  // receives exactly as many writes as it was counted, inside its own range
+  for (int il = 0; il < sel.n_qpages; ++il) {
+    for (int x = tid; x < per_qp; x += 1024) {
+      const int g = x / sel.stride, j = x % sel.stride;
+      int n = sel.count[(int64_t)il * hkv + g];
+      n = n < 0 ? 0 : (n > sel.stride ? sel.stride : n);
+      if (j < n) {
+        const int p = sel.pages[((int64_t)il * hkv + g) * sel.stride + j];
+        if (p >= 0 && p < pl.n_pages) {
+          const int e = g * pl.n_pages + p;
+          lst[off[e] + atomicAdd(&cnt[e], 1)] = il;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Dense: grid ceil(n_keys / 128) * hkv * splits, workgroup -> (KV head, slab,
+// split) with bid % Hkv = KV head (a head's workgroups share XCDs) and the
+// earliest slabs (the most query rows) first.  Sparse: grid = the work list's
+// capacity, workgroup b takes item b (or exits).  BQT: query rows per tile (32
+// or 64); OCC: waves per SIMD the register budget is sized for.
 template <int OCC, int BQT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 dkdv_bf16_kernel(AttnCall c, int splits) {
@@ -29,52 +129,53 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   __shared__ DkvSmem<BQT> sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  // Workgroup -> (KV head, slab, split): bid % Hkv = KV head keeps a head's
-  // workgroups on the same XCDs; the earliest slabs (the most query rows)
-  // first.
   const int bid = blockIdx.x;
-  const int g = bid % c.g.hkv;
-  const int m = bid / c.g.hkv;
-  const int slab = m / splits, zsplit = m % splits;
   const int G = c.hq / c.g.hkv;
   const int P = c.g.page;
+  const int tiles_pp = P / BQT;
   const int64_t n_keys = c.q_pos0 + c.n_q;
+
+  // This workgroup's KV head, 128-key slab and range [it0, it1) of its
+  // iterations; iteration it = head (it / n_rt) x row tile (it % n_rt) over the
+  // n_rt row tiles (BQT query rows) of the chunk that can see the slab.
+  int g, slab, it0, it1, n_rt, r_first = 0;
+  if (c.sel.pages) {
+    const int* pb = c.plan.base;
+    if (bid >= pb[0]) return;
+    const int4 item = reinterpret_cast<const int4*>(pb + c.plan.off_items)[bid];
+    g = uni(item.x);
+    slab = uni(item.y);
+    it0 = uni(item.z);
+    it1 = uni(item.w);
+    if (g < 0 || g >= c.g.hkv || slab < 0 || (int64_t)slab * 128 >= (int64_t)c.plan.n_pages * P ||
+        it0 < 0)
+      return;  // not a valid item (cannot happen for a plan written by dkdv_plan_kernel)
+    const int e = g * c.plan.n_pages + (int)((int64_t)slab * 128 / P);
+    int n = uni(pb[c.plan.off_cnt + e]);
+    n = n < 1024 ? n : 1024;  // at most one hit per query page
+    const int* lst = pb + c.plan.off_lst + pb[c.plan.off_off + e];
+    for (int i = tid; i < n; i += 256) sm.qpl[i] = lst[i];
+    __syncthreads();
+    n_rt = n * tiles_pp;
+    if (it1 > n_rt * G) it1 = n_rt * G;
+  } else {
+    g = bid % c.g.hkv;
+    const int m = bid / c.g.hkv;
+    slab = m / splits;
+    const int zsplit = m % splits;
+    r_first = (int)((int64_t)slab * 128 - c.q_pos0);
+    if (r_first < 0) r_first = 0;
+    r_first -= r_first % BQT;
+    n_rt = (c.n_q - r_first + BQT - 1) / BQT;
+    const int total = n_rt * G;
+    it0 = (int)((int64_t)total * zsplit / splits);
+    it1 = (int)((int64_t)total * (zsplit + 1) / splits);
+  }
+  if (it0 >= it1) return;
   const int64_t s_base = (int64_t)slab * 128;
   const int64_t kpage = s_base / P;
   const int64_t wk0 = s_base + 32 * w;            // this wave's first key
   const int s_rel = (int)(wk0 + l32 - c.q_pos0);  // this lane's key, relative to q_pos0
-  const int nqp = (c.n_q + P - 1) / P;
-  const int tiles_pp = P / BQT;
-
-  // Row tiles (BQT query rows) of the chunk that can see this key slab.
-  int n_rt, r_first = 0;
-  if (c.sel.pages) {
-    if (tid == 0) {
-      int n = 0;
-      for (int il = 0; il < nqp; ++il) {
-        const int32_t* lst = c.sel.pages + ((int64_t)il * c.g.hkv + g) * c.sel.stride;
-        const int cnt = sel_count(c, il, g);
-        int lo = 0, hi = cnt;
-        while (lo < hi) {  // ascending list: binary search for kpage
-          const int mid = (lo + hi) >> 1;
-          if (lst[mid] < kpage) lo = mid + 1; else hi = mid;
-        }
-        if (lo < cnt && lst[lo] == kpage) sm.qpl[n++] = il;
-      }
-      sm.n_qpl = n;
-    }
-    __syncthreads();
-    n_rt = sm.n_qpl * tiles_pp;
-  } else {
-    r_first = (int)(s_base - c.q_pos0);
-    if (r_first < 0) r_first = 0;
-    r_first -= r_first % BQT;
-    n_rt = (c.n_q - r_first + BQT - 1) / BQT;
-  }
-  const int total = n_rt * G;
-  const int it0 = (int)((int64_t)total * zsplit / splits);
-  const int it1 = (int)((int64_t)total * (zsplit + 1) / splits);
-  if (it0 >= it1) return;
 
   bf16x8 kf[8], vf[8];
   const int slot = uni(c.L.table[(int64_t)g * c.g.max_logical + kpage]);
@@ -215,7 +316,8 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
     wait_dma_and_sync();
   }
 
-  // One fp32 atomic add per gradient element into the pool.
+  // One fp32 atomic add per gradient element into the pool (measured faster
+  // than a plain read-add-write even where the workgroup owns the element).
   float* dkp = c.L.dk + (((int64_t)g * c.g.slots + slot) * P + (wk0 % P)) * D + l32;
   float* dvp = c.L.dv + (((int64_t)g * c.g.slots + slot) * P + (wk0 % P)) * D + l32;
 #pragma unroll
@@ -232,23 +334,69 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
 
 }  // namespace
 
+// PKV_DKDV: "1x32" / "1x64" (32- or 64-row query tiles)
+static bool dkdv_rows32() {
+  static const bool r = [] {
+    const char* v = getenv("PKV_DKDV");
+    return v && !strcmp(v, "1x32");
+  }();
+  return r;
+}
+
+// Query pages per work item of the sparse dK/dV kernel (PKV_DKDV_QPI overrides).
+static int dkdv_qpi() {
+  static const int q = [] {
+    const char* v = getenv("PKV_DKDV_QPI");
+    const int x = v ? atoi(v) : 0;
+    return x >= 1 && x <= 1024 ? x : 4;
+  }();
+  return q;
+}
+
+DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel_stride) {
+  (void)hq;
+  DkvPlan pl{};
+  const int64_t n_keys = q_pos0 + n_q;
+  pl.n_pages = (int)((n_keys + g.page - 1) / g.page);
+  pl.qpi = dkdv_qpi();
+  const int64_t nqp = (n_q + g.page - 1) / g.page;
+  const int64_t E = (int64_t)g.hkv * pl.n_pages;
+  pl.lst_cap = nqp * g.hkv * (sel_stride > 0 ? sel_stride : 0);
+  pl.off_cnt = 64;
+  pl.off_off = pl.off_cnt + E;
+  pl.off_lst = pl.off_off + E;
+  pl.off_items = ((pl.off_lst + pl.lst_cap + 3) / 4) * 4;
+  const int64_t H = pl.lst_cap;
+  const int64_t bound = (H + pl.qpi - 1) / pl.qpi + (H < E ? H : E);
+  pl.max_items = (int)((H < bound ? H : bound) * (g.page / 128));
+  pl.bytes = (pl.off_items + 4 * (int64_t)pl.max_items) * 4;
+  return pl;
+}
+
 hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
   hipError_t e = launch_delta(c, true, s);
   if (e != hipSuccess) return e;
   e = launch_dq_bf16(c, s);
   if (e != hipSuccess) return e;
-  const int64_t n_keys = c.q_pos0 + c.n_q;
-  const int n_slabs = (int)((n_keys + 127) / 128);
-  int splits = (2048 + n_slabs * c.g.hkv - 1) / (n_slabs * c.g.hkv);
-  if (splits < 1) splits = 1;
-  if (splits > 16) splits = 16;
-  // PKV_DKDV: "1x32" / "1x64" (32- or 64-row query tiles)
-  static const bool rows32 = [] {
-    const char* v = getenv("PKV_DKDV");
-    return v && !strcmp(v, "1x32");
-  }();
-  KernelTimer t(KT_DKDV, s);
-  const dim3 grid(n_slabs * c.g.hkv * splits);
+  const bool rows32 = dkdv_rows32();
+  const int G = c.hq / c.g.hkv;
+  int splits = 1;
+  dim3 grid;
+  KernelTimer t(KT_DKDV, s);  // the planning kernel counts as part of dK/dV
+  if (c.sel.pages) {
+    if (c.plan.max_items == 0) return hipSuccess;  // nothing selected
+    hipLaunchKernelGGL(dkdv_plan_kernel, dim3(1), dim3(1024), 0, s, c.sel, c.g.hkv, G, c.g.page,
+                       c.g.page / (rows32 ? 32 : 64), c.plan);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    grid = dim3(c.plan.max_items);
+  } else {
+    const int64_t n_keys = c.q_pos0 + c.n_q;
+    const int n_slabs = (int)((n_keys + 127) / 128);
+    splits = (2048 + n_slabs * c.g.hkv - 1) / (n_slabs * c.g.hkv);
+    if (splits < 1) splits = 1;
+    if (splits > 16) splits = 16;
+    grid = dim3(n_slabs * c.g.hkv * splits);
+  }
   if (rows32)
     hipLaunchKernelGGL((dkdv_bf16_kernel<1, 32>), grid, dim3(256), 0, s, c, splits);
   else

@@ -302,8 +302,12 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   if ((st = check_sel(pool, sel, n_q, "pkv_attn_bwd")) != PKV_OK) return st;
   if (cdiv(n_q, pool->desc.page_size) > 1024)
     return fail(PKV_EUNSUPPORTED, "pkv_attn_bwd: chunks of more than 1024 pages");
-  if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes,
-                           2 * (int64_t)n_q_heads * n_q * (int64_t)sizeof(float))) != PKV_OK)
+  // scratch: D and lse2 ([hq][n_q] fp32 each), then the sparse dK/dV work list
+  const int64_t dl_bytes = ((2 * (int64_t)n_q_heads * n_q * (int64_t)sizeof(float) + 255) / 256) * 256;
+  const bool plan = sel && pool->desc.kv_dtype == PKV_BF16;
+  DkvPlan pl{};
+  if (plan) pl = dkdv_plan_layout(geom(pool), n_q_heads, q_pos0, (int)n_q, sel->stride);
+  if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes, dl_bytes + pl.bytes)) != PKV_OK)
     return st;
   if ((st = pool_before_compute(pool, layer, stream)) != PKV_OK) return st;
   AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
@@ -314,6 +318,10 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   c.dq = dq;
   c.delta = (float*)pool->d_delta;
   c.lse2 = pool->desc.kv_dtype == PKV_BF16 ? c.delta + (int64_t)n_q_heads * n_q : nullptr;
+  if (plan) {
+    pl.base = reinterpret_cast<int*>((char*)pool->d_delta + dl_bytes);
+    c.plan = pl;
+  }
   hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_bwd_bf16(c, stream) : launch_bwd_f32(c, stream);
   if (e != hipSuccess) return hip_fail(e, "pkv_attn_bwd: launch");
   return pool_after_compute(pool, layer, stream);

@@ -36,6 +36,23 @@ struct SelDev {
   int stride;
 };
 
+// Work list of the sparse bf16 dK/dV kernel, built on the device by a planning
+// kernel from the selection (int32 words at base):
+//   [0]                  number of work items
+//   cnt  [hkv][n_pages]  query pages whose selection holds key page p (head g)
+//   off  [hkv][n_pages]  start of that ascending query-page list in lst
+//   lst  [lst_cap]
+//   items[max_items]     int4 {g, 128-key slab, first, end iteration}
+struct DkvPlan {
+  int* base;
+  int n_pages;  // key pages of the chunk's context
+  int qpi;      // query pages per work item
+  int64_t off_cnt, off_off, off_lst, off_items;
+  int64_t lst_cap;
+  int max_items;
+  int64_t bytes;
+};
+
 // Everything an attention launch needs.
 struct AttnCall {
   LayerDev L;
@@ -54,6 +71,7 @@ struct AttnCall {
   float* delta;  // D = rowsum(dO * O), [hq][n_q]
   float* lse2;   // lse * log2(e), [hq][n_q] (bf16 backward only)
   float* dq;
+  DkvPlan plan;  // sparse bf16 backward only
 };
 
 // Brackets one kernel launch with timing events when kernel timing is on
@@ -97,6 +115,8 @@ hipError_t launch_bwd_f32(const AttnCall& c, hipStream_t s);
 hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s);
 hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s);  // D, lse2, dQ, dK/dV
 hipError_t launch_dq_bf16(const AttnCall& c, hipStream_t s);   // dQ only (D, lse2 written)
+// Sizes of the sparse dK/dV work list for a chunk (base left null).
+DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel_stride);
 
 // ---- kernels in attn_common.hip
 hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s);
