@@ -122,6 +122,10 @@ class LayerBench:
                                 cfg.group) for c in range(len(self.chunks)))
 
     def run(self, steps: int, warmup: int):
+        """Step time of `steps` steps (the library's normal mode: dQ and dK/dV
+        side by side), then the per-kernel HIP-event times of `steps` more
+        steps with kernel timing on (dQ and dK/dV one after the other, so each
+        kernel's events bracket its own work)."""
         import torch
         pkv = self.pkv
         for i in range(warmup):
@@ -129,12 +133,15 @@ class LayerBench:
         if warmup == 0:
             self.step(keep_counts=True)
         torch.cuda.synchronize()
-        pkv.pkv_kernel_timing(True)
         t0 = time.perf_counter()
         for _ in range(steps):
             self.step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        pkv.pkv_kernel_timing(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
         ktimes = pkv.pkv_kernel_times()
         pkv.pkv_kernel_timing(False)
         return ms, ktimes
@@ -405,6 +412,8 @@ def main():
         "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                     for k, e in ktab.items()},
+        "kernel_timing": "HIP events on the launching stream over a second pass of the same steps "
+                         "(dQ and dK/dV then run one after the other)",
         "roofline": roofline,
     }
 

@@ -181,7 +181,11 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
  * [n_q][n_q_heads][d] fp32, overwritten) and ADDS dK, dV into the layer's
  * gradient pool with fp32 atomics (dK/dV of a multi-chunk run are the sum
  * of every chunk's contribution).  Uses a library-owned scratch buffer for
- * D = rowsum(dO * O), grown with hipMalloc when a larger chunk arrives. */
+ * D = rowsum(dO * O), grown with hipMalloc when a larger chunk arrives.  bf16
+ * pools run the dQ and dK/dV kernels side by side on a second, library-owned
+ * stream forked from and joined back into `stream` with events (capturable
+ * into a HIP graph); the call's work is complete, as seen from `stream`, when
+ * the join is reached. */
 pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
                         int32_t n_q_heads, float scale, const void* q, const void* o,
                         const void* dout, const float* lse, const pkv_sel* sel, float* dq,
@@ -268,7 +272,10 @@ typedef enum {
   PKV_KT_COUNT = 8
 } pkv_kernel_kind;
 
-/* enable != 0: clear the counters and start timing; 0: stop timing. */
+/* enable != 0: clear the counters and start timing; 0: stop timing.  While
+ * timing is on, pkv_attn_bwd runs its dQ and dK/dV kernels one after the other
+ * (otherwise side by side on a library stream) so that each kernel's events
+ * bracket its own work only. */
 pkv_status pkv_kernel_timing(int32_t enable);
 
 /* Wait for the recorded events, then write per-kind totals: total_ms[k] and

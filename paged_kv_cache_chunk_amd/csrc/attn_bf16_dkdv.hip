@@ -373,11 +373,39 @@ DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel
   return pl;
 }
 
-hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s) {
+// PKV_BWD_STREAMS=1 runs dQ and dK/dV one after the other on the caller's
+// stream.
+static bool bwd_one_stream() {
+  static const bool r = [] {
+    const char* v = getenv("PKV_BWD_STREAMS");
+    return v && !strcmp(v, "1");
+  }();
+  return r;
+}
+
+static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s);
+
+hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s, hipStream_t aux, hipEvent_t ev_fork,
+                           hipEvent_t ev_join) {
   hipError_t e = launch_delta(c, true, s);
   if (e != hipSuccess) return e;
-  e = launch_dq_bf16(c, s);
-  if (e != hipSuccess) return e;
+  // with kernel timing on, one after the other, so that each kernel's events
+  // bracket its own work only
+  if (!aux || bwd_one_stream() || kernel_timing_on()) {
+    if ((e = launch_dq_bf16(c, s)) != hipSuccess) return e;
+    return launch_dkdv(c, s);
+  }
+  // fork: dK/dV (the longer kernel) first on aux, dQ on s, then join
+  if ((e = hipEventRecord(ev_fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(aux, ev_fork, 0)) != hipSuccess) return e;
+  if ((e = launch_dkdv(c, aux)) != hipSuccess) return e;
+  if ((e = launch_dq_bf16(c, s)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ev_join, aux)) != hipSuccess) return e;
+  return hipStreamWaitEvent(s, ev_join, 0);
+}
+
+static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s) {
+  hipError_t e = hipSuccess;
   const bool rows32 = dkdv_rows32();
   const int G = c.hq / c.g.hkv;
   int splits = 1;

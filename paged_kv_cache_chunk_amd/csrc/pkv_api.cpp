@@ -322,7 +322,7 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
     pl.base = reinterpret_cast<int*>((char*)pool->d_delta + dl_bytes);
     c.plan = pl;
   }
-  hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_bwd_bf16(c, stream) : launch_bwd_f32(c, stream);
+  hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_bwd_bf16(c, stream, pool->s_aux, pool->ev_fork, pool->ev_join) : launch_bwd_f32(c, stream);
   if (e != hipSuccess) return hip_fail(e, "pkv_attn_bwd: launch");
   return pool_after_compute(pool, layer, stream);
 }

@@ -74,6 +74,9 @@ struct AttnCall {
   DkvPlan plan;  // sparse bf16 backward only
 };
 
+// Whether kernel timing (pkv_kernel_timing) is on.
+bool kernel_timing_on();
+
 // Brackets one kernel launch with timing events when kernel timing is on
 // (pkv_kernel_timing); a no-op otherwise.
 class KernelTimer {
@@ -113,7 +116,12 @@ hipError_t launch_bwd_f32(const AttnCall& c, hipStream_t s);
 
 // ---- kernels in attn_bf16_fwd.hip, attn_bf16_dq.hip, attn_bf16_dkdv.hip
 hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s);
-hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s);  // D, lse2, dQ, dK/dV
+// D, lse2, dQ, dK/dV; dK/dV runs on `aux` (forked from s after D / lse2 with
+// ev_fork, joined back into s with ev_join) while dQ runs on s, so that the
+// two kernels fill each other's last partial wave of workgroups.  aux may be
+// null: everything on s.
+hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s, hipStream_t aux, hipEvent_t ev_fork,
+                           hipEvent_t ev_join);
 hipError_t launch_dq_bf16(const AttnCall& c, hipStream_t s);   // dQ only (D, lse2 written)
 // Sizes of the sparse dK/dV work list for a chunk (base left null).
 DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel_stride);

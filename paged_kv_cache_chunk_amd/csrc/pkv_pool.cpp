@@ -68,6 +68,11 @@ pkv_status pool_allocate(pkv_pool* p) {
   if ((st = dev_alloc(p, (void**)&p->d_table, tabb, "device allocation of the page tables failed")) != PKV_OK) return st;
   hipError_t e = hipMemcpy(p->d_table, p->h_table.data(), (size_t)tabb, hipMemcpyHostToDevice);
   if (e != hipSuccess) return pool_hip_fail(e, "hipMemcpy (page tables)");
+  if ((e = hipStreamCreateWithFlags(&p->s_aux, hipStreamNonBlocking)) != hipSuccess)
+    return pool_hip_fail(e, "hipStreamCreate");
+  if ((e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventCreate");
   if (d.host_tier) {
     if ((st = dev_alloc(p, (void**)&p->d_need, needb, "device allocation of the window map failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_moved, 16, "device allocation of the copy counters failed")) != PKV_OK) return st;
@@ -119,6 +124,9 @@ pkv_status pool_release(pkv_pool* p) {
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
     for (void* x : *v)
       if (x) (void)hipHostFree(x);
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+  if (p->ev_join) (void)hipEventDestroy(p->ev_join);
+  if (p->s_aux) (void)hipStreamDestroy(p->s_aux);
   for (int w = 0; w < pkv_pool::kWindow; ++w) {
     if (p->ev_compute[w]) (void)hipEventDestroy(p->ev_compute[w]);
     if (p->ev_ready[w]) (void)hipEventDestroy(p->ev_ready[w]);

@@ -26,6 +26,10 @@ struct pkv_pool {
   float* d_reps = nullptr;        // [layers][Hkv][slots][d]
   int32_t* d_table = nullptr;     // [layers][Hkv][max_logical]
   void* d_delta = nullptr;        // attn_bwd scratch
+  // attn_bwd (bf16) runs dQ and dK/dV side by side: dK/dV on this stream,
+  // forked from and joined back to the caller's stream with the two events
+  hipStream_t s_aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int64_t delta_bytes = 0;
   void* d_select = nullptr;       // select scratch
   int64_t select_bytes = 0;

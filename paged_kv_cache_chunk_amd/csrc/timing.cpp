@@ -46,6 +46,8 @@ void resolve() {
 
 }  // namespace
 
+bool kernel_timing_on() { return g_on; }
+
 KernelTimer::KernelTimer(int kind, hipStream_t s) : kind_(kind), s_(s), start_(nullptr) {
   if (!g_on) return;
   hipEvent_t e = get_event();
