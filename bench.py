@@ -162,6 +162,26 @@ def kernel_table(lb: LayerBench, ms_step: float, ktimes: dict, steps: int) -> di
     return out
 
 
+def gemm_peak_tflops(n: int = 8192, reps: int = 20) -> float:
+    """bf16 GEMM rate of the box's BLAS (torch.matmul of two contiguous
+    n x n bf16 matrices, fp32 accumulate): a measured ceiling for dense bf16
+    MFMA work at the clock the chip holds under that load, reported beside the
+    2.5 PFLOP/s data-sheet figure."""
+    import torch
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def cpu_baseline(lb: LayerBench, rows: int) -> dict:
     """The fp64 oracle on a bounded sample of the workload: the last `rows`
     query rows of the context (all heads), forward + backward against every
@@ -416,6 +436,11 @@ def main():
                          "(dQ and dK/dV then run one after the other)",
         "roofline": roofline,
     }
+
+    gemm = gemm_peak_tflops()
+    line["gemm_bf16_tflops"] = round(gemm, 1)
+    line["mfma_frac_of_gemm"] = round(flops / ms / 1e9 / gemm, 4)
+    log(f"[bench] bf16 GEMM (8192^3, torch.matmul): {gemm:.1f} TFLOP/s")
 
     if args.sparse_workload and args.sparse_workload != "none":
         scfg = get_config(args.sparse_workload)
