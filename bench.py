@@ -281,6 +281,7 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
             list(reversed(range(cfg.n_chunks)))
         pkv.pkv_kernel_timing(True)
         torch.cuda.synchronize()
+        windows = []  # (first chunk id of the window, chunks done, bytes fetched, written) so far
         t0 = time.perf_counter()
         for n_done, c in enumerate(chunk_ids):
             n = cfg.chunk_range(c)[1]
@@ -291,8 +292,11 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
             sweep.chunk(c, inputs, bufs)
             if n_done % 8 == 7:
                 torch.cuda.synchronize()
+                fb, wb = pkv.pkv_offload_bytes(pool)
+                windows.append((c, n_done + 1, fb, wb))
                 log(f"[bench] {cfg.name} {mode}: backward sweep chunk {n_done + 1}/"
-                    f"{len(chunk_ids)}, {time.perf_counter() - t0:.1f}s")
+                    f"{len(chunk_ids)}, {time.perf_counter() - t0:.1f}s, "
+                    f"fetched {fb / 1e9:.1f} GB, written back {wb / 1e9:.1f} GB")
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         kt = pkv.pkv_kernel_times()
@@ -300,7 +304,16 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
         fetched, written = pkv.pkv_offload_bytes(pool)
         compute = sum(kt[k][0] for k in ("select", "fwd", "delta", "dq", "dkdv")) / 1e3
         copy = sum(kt[k][0] for k in ("fetch", "writeback")) / 1e3
+        per_window = []
+        prev = (0, 0, 0)
+        for c_last, done, fb, wb in windows:
+            n = done - prev[0]
+            per_window.append({"chunks": f"{c_last + n - 1}..{c_last}",
+                               "fetched_gb_per_layer_chunk": round((fb - prev[1]) / 1e9 / (n * L), 3),
+                               "written_gb_per_layer_chunk": round((wb - prev[2]) / 1e9 / (n * L), 3)})
+            prev = (done, fb, wb)
         results[mode] = {"wall_s": wall, "compute_kernels_s": compute, "copy_kernels_s": copy,
+                         "per_window": per_window,
                          "fetched_bytes": fetched, "written_bytes": written,
                          "chunks": len(chunk_ids), "hbm_bytes": dev_b, "host_bytes": host_b,
                          "kernels": {k: round(v[0], 1) for k, v in kt.items() if v[1]}}
@@ -311,9 +324,10 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
     tokens = sum(cfg.chunk_range(c)[1] for c in (list(reversed(range(cfg.n_chunks)))[:steps]
                                                   if steps > 0 else range(cfg.n_chunks)))
     out = {
-        "workload": f"{cfg.name}: {L} layers, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, top-K "
-                    f"{cfg.top_k} + {cfg.n_sink} sink + {cfg.n_local} local pages, K/V and "
-                    f"gradient pools in pinned host memory (bf16), HBM window of 2 layers",
+        "workload": f"{cfg.name}: {L} layers, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, "
+                    + (f"top-K {cfg.top_k} + {cfg.n_sink} sink + {cfg.n_local} local pages"
+                       if cfg.sparse else "dense causal")
+                    + ", K/V and gradient pools in pinned host memory (bf16), HBM window of 2 layers",
         "chunks_timed": off["chunks"],
         "tokens_per_s_per_layer": round(tokens * L / off["wall_s"], 1),
         "backward_sweep_s": round(off["wall_s"], 3),
@@ -329,6 +343,7 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
         "hbm_gib": round(off["hbm_bytes"] / 2**30, 3),
         "host_gib": round(off["host_bytes"] / 2**30, 3),
         "kernels_ms": off["kernels"],
+        "bytes_per_8_chunks": off["per_window"],
     }
     if "resident" in results:
         res_s = results["resident"]["wall_s"]
@@ -391,7 +406,8 @@ def main():
         if args.layers:
             cfg = cfg.replace(n_layers=args.layers)
         res = offload_bench(cfg, args.chunks, args.resident_ab)
-        res.update({"metric": "offloaded top-K stack: backward-sweep tokens/s per layer",
+        res.update({"metric": f"offloaded {'top-K' if cfg.sparse else 'dense'} stack: "
+                              "backward-sweep tokens/s per layer",
                     "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(res), flush=True)
         return

@@ -82,6 +82,12 @@ CONFIGS = {
     "qwen_256k_topk": Config("qwen_256k_topk", 1, 262144, 4096, 128, dtype="bf16",
                              slots=2048, table="permutation", sparse=True, top_k=64,
                              planted_frac=0.05, planted_norm=2.0, cid=3, **QWEN),
+    # 28 layers of the 128K dense workload with every layer's pools in pinned host
+    # memory and a 16 GiB HBM cap (the dense offloaded stack).
+    "qwen_128k_dense_offload": Config("qwen_128k_dense_offload", 28, 131072, 12288, 128,
+                                      dtype="bf16", slots=1024, table="permutation",
+                                      rope_base=1e6, do_scale=1.0 / 64.0, host_tier=True,
+                                      hbm_cap_bytes=16 << 30, cid=5, **QWEN),
     # 28 layers, 1M tokens, top-K 128, pools in pinned host memory, 16 GiB HBM cap.
     "qwen_1m_offload": Config("qwen_1m_offload", 28, 1048576, 8192, 128, dtype="bf16",
                               slots=8192, table="permutation", sparse=True, top_k=128,
