@@ -93,7 +93,9 @@ class LayerBench:
                 self.bufs[n] = ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page, dt, self.sparse)
         self.sel_counts = {}
 
-    def step(self, keep_counts: bool = False):
+    def step(self, keep_counts: bool = False, on_chunk=None):
+        """One layer step; on_chunk(c, buffers) is called after chunk c's
+        backward is enqueued (the buffers are reused by the next chunk)."""
         pkv, cfg = self.pkv, self.cfg
         pkv.pkv_pool_reset(self.pool, 0)
         pkv.pkv_grad_zero(self.pool, 0)
@@ -111,6 +113,8 @@ class LayerBench:
             pkv.pkv_attn_fwd(self.pool, 0, ch["q_pos0"], ch["q"], b.o, b.lse, cfg.scale, sel=b.sel)
             pkv.pkv_attn_bwd(self.pool, 0, ch["q_pos0"], ch["q"], b.o, ch["do"], b.lse, b.dq,
                              cfg.scale, sel=b.sel)
+            if on_chunk is not None:
+                on_chunk(c, b)
 
     def pairs(self) -> int:
         """Attended (query, key) pairs summed over query heads, one step."""
@@ -160,6 +164,57 @@ def kernel_table(lb: LayerBench, ms_step: float, ktimes: dict, steps: int) -> di
             e["tflops"] = fl * steps / (tot * 1e-3) / 1e12
         out[k] = e
     return out
+
+
+def topk_sweep(name: str, budgets, sample_chunks=(63, 40, 16), steps: int = 2) -> list:
+    """Step time and the error of the top-K restriction against dense causal
+    attention on the same inputs, for several top-K budgets: O and dQ of the
+    sampled chunks and the whole dK/dV pool, max |sparse - dense| / max
+    |dense|.  Both sides are library outputs (each pinned to the oracle by
+    the parity tests); the selection is held constant in the gradients."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    base = get_config_checked(name)
+
+    def run(cfg):
+        lb = LayerBench(cfg)
+        ms, _ = lb.run(steps, 1)
+        keep = {}
+
+        def grab(c, b):
+            if c in sample_chunks:
+                keep[c] = (b.o.float().clone(), b.dq.clone())
+        lb.step(on_chunk=grab)
+        n = cfg.n_ctx
+        dk = torch.empty(n, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        pkv.pkv_read_pages(lb.pool, 0, pkv.PKV_DK, dk)
+        pkv.pkv_read_pages(lb.pool, 0, pkv.PKV_DV, dv)
+        torch.cuda.synchronize()
+        pairs = lb.pairs()
+        lb.pool.close()
+        del lb
+        return ms, pairs, keep, dk, dv
+
+    def rel(a, b):
+        return float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))
+
+    d_ms, d_pairs, d_keep, d_dk, d_dv = run(base.replace(name=f"{name}@dense", sparse=False))
+    out = [{"top_k": "dense", "ms_per_step": round(d_ms, 3), "pairs_frac": 1.0}]
+    for k in budgets:
+        ms, pairs, keep, dk, dv = run(base.replace(name=f"{name}@K{k}", top_k=k))
+        err = {"O": max(rel(keep[c][0], d_keep[c][0]) for c in keep),
+               "dq": max(rel(keep[c][1], d_keep[c][1]) for c in keep),
+               "dk": rel(dk, d_dk), "dv": rel(dv, d_dv)}
+        out.append({"top_k": k, "ms_per_step": round(ms, 3), "pairs_frac": round(pairs / d_pairs, 4),
+                    "rel_err_vs_dense": {e: round(v, 4) for e, v in err.items()}})
+        log(f"[bench] top-K sweep {name} K={k}: {out[-1]}")
+    return out
+
+
+def get_config_checked(name: str):
+    from synthetic import get_config
+    return get_config(name)
 
 
 def gemm_peak_tflops(n: int = 8192, reps: int = 20) -> float:
@@ -373,6 +428,9 @@ def main():
                     help="offloaded workload: time only the last N chunks of the backward sweep")
     ap.add_argument("--resident-ab", action="store_true",
                     help="offloaded workload: also run the same sweep with all pools in HBM")
+    ap.add_argument("--topk-sweep", default="", metavar="K1,K2,..",
+                    help="only run the top-K budget sweep on --workload (a top-K workload): "
+                         "step time and error against dense attention per budget")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -402,6 +460,13 @@ def main():
         sys.exit(1)
 
     cfg = get_config(args.workload)
+    if args.topk_sweep:
+        budgets = [int(x) for x in args.topk_sweep.split(",")]
+        res = topk_sweep(args.workload, budgets)
+        print(json.dumps({"metric": "top-K budget sweep: step ms and error vs dense",
+                          "workload": args.workload, "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "results": res}), flush=True)
+        return
     if cfg.host_tier:
         if args.layers:
             cfg = cfg.replace(n_layers=args.layers)

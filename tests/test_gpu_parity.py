@@ -135,3 +135,26 @@ def test_f32_partial_page_tail():
     got = run_layer(cfg, w)
     _, ref = _oracle_for(cfg, w)
     _check(cfg, got, ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 4)])
+def test_bf16_local_window_mode(n_sink, n_local):
+    """top_k = 0: the selection is the forced pages only (sink pages and a
+    window of the n_local most recent pages), i.e. sliding-window attention
+    with attention sinks; no scoring is involved, so the lists are exact."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    cfg = mini_config("qwen_256k_topk", n_ctx=3072, chunk=1024, top_k=0, n_sink=n_sink,
+                      n_local=n_local)
+    sp = Sparse(top_k=0, n_sink=n_sink, n_local=n_local)
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f, ref = _oracle_for(cfg, w, sp)
+    for c in range(cfg.n_chunks):
+        q_pos0, n = cfg.chunk_range(c)
+        pages, count = got["sel"][c]
+        for il in range(pages.shape[0]):
+            i = q_pos0 // cfg.page + il
+            want = sorted(set(range(min(n_sink, i + 1))) | set(range(max(0, i - n_local + 1), i + 1)))
+            for g in range(cfg.hkv):
+                assert list(pages[il, g, :count[il, g]]) == want
+    _check(cfg, got, ref, TOL["bf16"])
