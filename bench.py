@@ -217,6 +217,54 @@ def get_config_checked(name: str):
     return get_config(name)
 
 
+def phase_rates(lb: "LayerBench", reps: int = 3) -> dict:
+    """Data movement of two phases on the largest chunk of a dense workload,
+    without arithmetic (libpkv measurement kernels), beside the attention
+    kernels of the same chunk:
+      * the forward's K/V tile stream into LDS: pkv_measure_gather vs
+        pkv_attn_fwd, bytes = the tiles streamed (64 keys x 256 B, K and V,
+        per query block and head);
+      * the dK/dV atomic epilogue: pkv_measure_atomics over every key, bytes
+        = 4 B per fp32 atomic add (dK and dV)."""
+    import torch
+    pkv, cfg = lb.pkv, lb.cfg
+    c = max(range(len(lb.chunks)), key=lambda i: lb.chunks[i]["q_pos0"] * lb.chunks[i]["q"].shape[0])
+    ch = lb.chunks[c]
+    q_pos0, n_q = ch["q_pos0"], ch["q"].shape[0]
+    b = lb.bufs[n_q]
+    nqb = -(-n_q // 128)
+    tiles = sum((q_pos0 + min(r0 + 128, n_q) - 1 + 64) // 64 for r0 in range(0, n_q, 128))
+    gather_bytes = tiles * cfg.hq * 64 * 256 * 2
+    out = torch.empty(nqb * cfg.hq, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_g = timed(lambda: pkv.pkv_measure_gather(lb.pool, 0, q_pos0, n_q, cfg.hq, out))
+    t_f = timed(lambda: pkv.pkv_attn_fwd(lb.pool, 0, q_pos0, ch["q"], b.o, b.lse, cfg.scale))
+    n_keys = cfg.n_ctx
+    a_reps = 8
+    t_a = timed(lambda: pkv.pkv_measure_atomics(lb.pool, 0, n_keys, a_reps))
+    atom_bytes = n_keys * cfg.hkv * cfg.d * 4 * 2 * a_reps
+    pkv.pkv_grad_zero(lb.pool, 0)
+    torch.cuda.synchronize()
+    return {"chunk": f"rows {q_pos0}..{q_pos0 + n_q - 1}",
+            "gather": {"tile_bytes": gather_bytes, "ms": round(t_g, 3),
+                       "gb_per_s": round(gather_bytes / t_g / 1e6, 1),
+                       "fwd_ms_same_chunk": round(t_f, 3),
+                       "fwd_tile_gb_per_s": round(gather_bytes / t_f / 1e6, 1)},
+            "atomics": {"adds": n_keys * cfg.hkv * cfg.d * 2 * a_reps, "ms": round(t_a, 3),
+                        "gb_per_s": round(atom_bytes / t_a / 1e6, 1)}}
+
+
 def gemm_peak_tflops(n: int = 8192, reps: int = 20) -> float:
     """bf16 GEMM rate of the box's BLAS (torch.matmul of two contiguous
     n x n bf16 matrices, fp32 accumulate): a measured ceiling for dense bf16
@@ -518,6 +566,8 @@ def main():
         "roofline": roofline,
     }
 
+    line["phases"] = phase_rates(lb)
+    log(f"[bench] phases: {line['phases']}")
     gemm = gemm_peak_tflops()
     line["gemm_bf16_tflops"] = round(gemm, 1)
     line["mfma_frac_of_gemm"] = round(flops / ms / 1e9 / gemm, 4)

@@ -285,6 +285,30 @@ pkv_status pkv_kernel_times(int32_t n, double* total_ms, int64_t* launches);
 /* Bytes the pool holds on the device and in pinned host memory. */
 pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* host_bytes);
 
+/* ---- Measurement kernels (not used by the attention path).  They move the
+ * data of one phase of the bf16 path without its arithmetic, so that the
+ * attention kernels' rates can be set beside the rate of their memory
+ * traffic alone.  bf16 pools without a host tier (else PKV_EUNSUPPORTED).
+ *
+ * pkv_measure_gather: streams into LDS exactly the K/V tiles that
+ * pkv_attn_fwd(layer, q_pos0, n_q, n_q_heads, sel) reads (same grid, tile
+ * walk, page-table lookups and double buffering; "Out of the Memory
+ * Barrier", gist.science de, section 2.B: attention reads K/V page by page
+ * through the table) and computes nothing.  out: caller-owned device buffer
+ * of ceil(n_q / 128) * n_q_heads floats (one word per workgroup, contents
+ * unspecified).  Same argument checks as pkv_attn_fwd.
+ *
+ * pkv_measure_atomics: adds `value` `reps` times to every dK and dV element
+ * of keys [0, n_keys) of `layer` with the lane pattern of the dK/dV kernel's
+ * fp32 atomic epilogue (de section 2.B: in-place atomic accumulation of the
+ * KV gradients).  Modifies the gradient pool (zero it afterwards with
+ * pkv_grad_zero); n_keys <= pkv_length(layer), reps >= 0. */
+pkv_status pkv_measure_gather(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                              int32_t n_q_heads, const pkv_sel* sel, float* out,
+                              hipStream_t stream);
+pkv_status pkv_measure_atomics(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t reps,
+                               float value, hipStream_t stream);
+
 /* Thread-local message of the last non-OK status returned on this thread. */
 const char* pkv_last_error(void);
 

@@ -26,7 +26,7 @@ EXPORTS = (
     "pkv_append_kv", "pkv_attn_fwd", "pkv_attn_bwd", "pkv_select_topk_pages",
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
     "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
-    "pkv_kernel_times", "pkv_offload_bytes",
+    "pkv_kernel_times", "pkv_offload_bytes", "pkv_measure_gather", "pkv_measure_atomics",
 )
 KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "pkv_grad_zero": [P, I32, VP],
             "pkv_read_pages": [P, I32, I32, VP, VP],
             "pkv_pool_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+            "pkv_measure_gather": [P, I32, I64, I64, I32, ctypes.POINTER(pkv_sel), VP, VP],
+            "pkv_measure_atomics": [P, I32, I64, I32, F, VP],
             "pkv_pool_reset": [P, I32],
             "pkv_offload_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
             "pkv_kernel_timing": [I32],
@@ -256,6 +258,19 @@ def pkv_kernel_times() -> dict:
     cnt = (ctypes.c_int64 * n)()
     _check(lib().pkv_kernel_times(n, ms, cnt))
     return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def pkv_measure_gather(pool: Pool, layer: int, q_pos0: int, n_q: int, n_q_heads: int, out,
+                       sel=None, stream=None) -> None:
+    """Measurement kernel: stream the K/V tiles pkv_attn_fwd would read, no math."""
+    _check(lib().pkv_measure_gather(pool.handle, layer, q_pos0, n_q, n_q_heads, _selp(sel),
+                                    _ptr(out), _stream(stream)))
+
+
+def pkv_measure_atomics(pool: Pool, layer: int, n_keys: int, reps: int, value: float = 0.0,
+                        stream=None) -> None:
+    """Measurement kernel: the dK/dV atomic epilogue over keys [0, n_keys), reps times."""
+    _check(lib().pkv_measure_atomics(pool.handle, layer, n_keys, reps, value, _stream(stream)))
 
 
 def pkv_last_error() -> str:

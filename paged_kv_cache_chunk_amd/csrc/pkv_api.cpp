@@ -327,6 +327,39 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   return pool_after_compute(pool, layer, stream);
 }
 
+pkv_status pkv_measure_gather(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                              int32_t n_q_heads, const pkv_sel* sel, float* out,
+                              hipStream_t stream) {
+  pkv_status st = check_attn(pool, layer, q_pos0, n_q, n_q_heads, "pkv_measure_gather");
+  if (st != PKV_OK) return st;
+  if (pool->desc.kv_dtype != PKV_BF16 || pool->desc.host_tier)
+    return fail(PKV_EUNSUPPORTED, "pkv_measure_gather: bf16 pools without a host tier only");
+  if (n_q == 0) return PKV_OK;
+  if (!out) return fail(PKV_EINVAL, "pkv_measure_gather: null out");
+  if ((st = check_sel(pool, sel, n_q, "pkv_measure_gather")) != PKV_OK) return st;
+  AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, 1.f, sel);
+  hipError_t e = launch_micro_gather(c, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "pkv_measure_gather: launch");
+  return PKV_OK;
+}
+
+pkv_status pkv_measure_atomics(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t reps,
+                               float value, hipStream_t stream) {
+  if (!pool) return fail(PKV_EINVAL, "pkv_measure_atomics: null pool");
+  if (layer < 0 || layer >= pool->desc.n_layers)
+    return fail(PKV_EINVAL, "pkv_measure_atomics: layer %d out of range", layer);
+  if (pool->desc.kv_dtype != PKV_BF16 || pool->desc.host_tier)
+    return fail(PKV_EUNSUPPORTED, "pkv_measure_atomics: bf16 pools without a host tier only");
+  if (n_keys < 0 || n_keys > pool->length[layer] || reps < 0)
+    return fail(PKV_EINVAL, "pkv_measure_atomics: n_keys=%lld (layer holds %lld), reps=%d",
+                (long long)n_keys, (long long)pool->length[layer], reps);
+  if (n_keys == 0 || reps == 0) return PKV_OK;
+  AttnCall c = make_call(pool, layer, 0, n_keys, pool->desc.n_kv_heads, 1.f, nullptr);
+  hipError_t e = launch_micro_atomics(c, reps, value, stream);
+  if (e != hipSuccess) return hip_fail(e, "pkv_measure_atomics: launch");
+  return PKV_OK;
+}
+
 pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
                                  int32_t n_q_heads, const void* q, int32_t top_k,
                                  int32_t n_sink, int32_t n_local, int32_t* sel_pages,

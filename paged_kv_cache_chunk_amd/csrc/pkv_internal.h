@@ -126,6 +126,10 @@ hipError_t launch_dq_bf16(const AttnCall& c, hipStream_t s);   // dQ only (D, ls
 // Sizes of the sparse dK/dV work list for a chunk (base left null).
 DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel_stride);
 
+// ---- measurement kernels in micro.hip (not used by the attention path)
+hipError_t launch_micro_gather(const AttnCall& c, float* out, hipStream_t s);
+hipError_t launch_micro_atomics(const AttnCall& c, int reps, float value, hipStream_t s);
+
 // ---- kernels in attn_common.hip
 hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s);
 
