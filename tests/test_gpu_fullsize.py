@@ -151,3 +151,93 @@ def test_qwen_256k_topk_full():
     picked = (1, 20, 63)
     got = _run(cfg, lambda n: [128, 2049], None, sel_chunks=picked)
     _check(cfg, got, heads=(0, 15), key_tail=32, sel_chunks=picked)
+
+
+def test_qwen_1m_offload_last_chunk():
+    """The 1M-token top-K workload with every pool in the host tier (2 of its
+    28 layers: the per-layer path is the same for every layer, and the box
+    pins at most 64 GiB per process): the backward sweep of the last chunk
+    through OffloadSweep (select one layer ahead, prefetch on a side stream,
+    gradient writeback), checked per layer against the oracle on the
+    selection of the chunk, sampled rows (O, LSE, dQ) and the last keys'
+    dK/dV in full, which only the last chunk's rows reach."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
+    from synthetic.gpu import GpuWorkload
+
+    cfg = get_config("qwen_1m_offload").replace(n_layers=2)
+    L, c_last = cfg.n_layers, cfg.n_chunks - 1
+    ws = [GpuWorkload(cfg, layer=l) for l in range(L)]
+    pool = pkv.pkv_pool_create(L, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16,
+                               host_tier=1, host_grad_dtype=pkv.PKV_BF16,
+                               device_budget_bytes=cfg.hbm_cap_bytes)
+    for l in range(L):
+        tab = ws[l].table()
+        for g in range(cfg.hkv):
+            pkv.pkv_page_table_set(pool, l, g, tab[g])
+    host_k = [[] for _ in range(L)]
+    host_v = [[] for _ in range(L)]
+    for c in range(cfg.n_chunks):
+        for l in range(L):
+            kv = ws[l].chunk(c, "kv")
+            pkv.pkv_append_kv(pool, l, kv["q_pos0"], kv["k"], kv["v"])
+            host_k[l].append(kv["k"].float().cpu().numpy())
+            host_v[l].append(kv["v"].float().cpu().numpy())
+    sp = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local)
+    sweep = OffloadSweep(pool, L, cfg.hq, cfg.hkv, cfg.d, cfg.page, cfg.scale, sp, torch.bfloat16)
+    ins = {l: ws[l].chunk(c_last, "qd") for l in range(L)}
+    n = ins[0]["q"].shape[0]
+    bufs = {l: ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page, torch.bfloat16, sp)
+            for l in range(L)}
+    rows = sorted({0, 1, 127, 128, n // 2, n - 1})
+    got = {}
+
+    def outputs(l, c, b):
+        ri = torch.tensor(rows, device="cuda")
+        got[l] = dict(O=b.o[ri].float().cpu().numpy(), lse=b.lse[:, ri].cpu().numpy(),
+                      dq=b.dq[ri].cpu().numpy(),
+                      sel=(b.sel[0].cpu().numpy(), b.sel[1].cpu().numpy()))
+
+    sweep.chunk(c_last, lambda l, c: ins[l], bufs, outputs)
+    torch.cuda.synchronize()
+    N, tail = cfg.n_ctx, 32
+    worst = {}
+    for l in range(L):
+        dk = torch.empty(N, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        pkv.pkv_read_pages(pool, l, pkv.PKV_DK, dk)
+        pkv.pkv_read_pages(pool, l, pkv.PKV_DV, dv)
+        torch.cuda.synchronize()
+        k = np.concatenate(host_k[l])
+        v = np.concatenate(host_v[l])
+        q = ins[l]["q"].float().cpu().numpy()
+        do = ins[l]["do"].float().cpu().numpy()
+        q_pos0 = ins[l]["q_pos0"]
+        ref_sel, scores = oracle.select_pages(q, k, q_pos0, cfg.page, cfg.hkv, cfg.top_k,
+                                              cfg.n_sink, cfg.n_local, score_dtype=np.float32,
+                                              return_scores=True)
+        nd = compare_selection(sel_lists(got[l]["sel"]), ref_sel, scores, cfg.top_k)
+        assert nd == 0, f"layer {l}: {nd} selections differ (inside the score gap)"
+        t_abs = q_pos0 + np.array(rows)
+        for h in (0, 15, 27):
+            ok = np.zeros((len(rows), cfg.n_pages), dtype=bool)
+            for i, r in enumerate(rows):
+                ok[i, ref_sel[r // cfg.page][h // cfg.group]] = True
+            O, lse, dq = oracle.rows_fwd_bwd(q[rows, h], do[rows, h], t_abs, h, k, v, cfg.scale,
+                                             cfg.group, cfg.page, ok)
+            worst[f"O{l}"] = max(worst.get(f"O{l}", 0.0), rel_err(got[l]["O"][:, h], O))
+            worst[f"lse{l}"] = max(worst.get(f"lse{l}", 0.0), rel_err(got[l]["lse"][h], lse))
+            worst[f"dq{l}"] = max(worst.get(f"dq{l}", 0.0), rel_err(got[l]["dq"][:, h], dq))
+        s0 = N - tail
+        off = s0 - q_pos0
+        rdk, rdv = oracle.key_grads_sampled(s0, q[off:], do[off:], k, v, cfg.scale, cfg.chunk,
+                                            cfg.page, {c_last: ref_sel})
+        # bf16 host gradient tier: the tail's grads made one bf16 round trip
+        worst[f"dk_tail{l}"] = rel_err(dk.cpu().numpy()[s0:], rdk)
+        worst[f"dv_tail{l}"] = rel_err(dv.cpu().numpy()[s0:], rdv)
+        del k, v
+    pool.close()
+    print(cfg.name, {k_: f"{v_:.2e}" for k_, v_ in worst.items()}, flush=True)
+    for name, e in worst.items():
+        assert e <= 1e-2, f"{name}: {e:.3e}"
