@@ -158,3 +158,26 @@ def test_bf16_local_window_mode(n_sink, n_local):
             for g in range(cfg.hkv):
                 assert list(pages[il, g, :count[il, g]]) == want
     _check(cfg, got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("hq,hkv,page,sparse_k", [
+    (8, 2, 256, 0),    # pages of 256 tokens (two 128-key slabs per page), G = 4
+    (8, 2, 256, 3),    # the same in top-K mode
+    (4, 4, 128, 0),    # multi-head attention (G = 1)
+    (16, 1, 128, 2),   # one KV head for 16 query heads, top-K
+])
+def test_bf16_other_shapes(hq, hkv, page, sparse_k):
+    """bf16 kernels at head ratios and page sizes other than the Qwen
+    shape's, with a ragged last chunk, against the oracle."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    base = "qwen_256k_topk" if sparse_k else "qwen_32k_dense"
+    n_ctx = 10 * page + page // 2 + 32
+    cfg = mini_config(base, n_ctx=n_ctx, chunk=4 * page, hq=hq, hkv=hkv, page=page,
+                      top_k=sparse_k)
+    sp = Sparse(top_k=sparse_k) if sparse_k else None
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f, ref = _oracle_for(cfg, w, sp)
+    if sp is not None:
+        _check_sel(cfg, f, got, ref, sp)
+    _check(cfg, got, ref, TOL["bf16"])
