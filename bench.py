@@ -265,6 +265,63 @@ def phase_rates(lb: "LayerBench", reps: int = 3) -> dict:
                         "gb_per_s": round(atom_bytes / t_a / 1e6, 1)}}
 
 
+def block_bench(n_ctx: int, chunk: int, top_k: int = 0) -> dict:
+    """Chunk-recurrent training of one random-initialised Qwen2.5-7B-shaped
+    attention block (hidden 3584, Hq 28, Hkv 4, d 128, RoPE base 1e6; bf16
+    products, fp32 master weights): forward sweep (appends), backward sweep
+    (recompute + attention backward into the pool + the chunks' K/V
+    gradients back through W_k, W_v).  Reports time, the attention kernels'
+    share, and memory: pool bytes per token and each sweep's transient working
+    set (the torch allocator's peak above what stays allocated after it)."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    from paged_kv_cache_chunk_amd.recurrent import AttentionBlock
+
+    torch.cuda.empty_cache()
+    sparse = Sparse(top_k) if top_k else None
+    block = AttentionBlock(max_tokens=n_ctx, sparse=sparse, seed=0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    xs, gys = [], []
+    for p0 in range(0, n_ctx, chunk):
+        n = min(chunk, n_ctx - p0)
+        xs.append(torch.randn(n, block.hidden, generator=g, device="cuda").to(torch.bfloat16))
+        gys.append((torch.randn(n, block.hidden, generator=g, device="cuda") / 64).to(torch.bfloat16))
+    block.forward_sweep(xs)      # warm-up
+    block.backward_sweep(xs, gys)
+    for w in block.parameters():
+        w.grad = None
+    torch.cuda.synchronize()
+    pkv.pkv_kernel_timing(True)
+    # transient working set of a sweep = its peak above what stays allocated
+    # after it (inputs, outputs kept for the caller, weights and their grads)
+    torch.cuda.reset_peak_memory_stats()
+    t0 = time.perf_counter()
+    ys = block.forward_sweep(xs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ws_fwd = torch.cuda.max_memory_allocated() - torch.cuda.memory_allocated()
+    del ys
+    torch.cuda.reset_peak_memory_stats()
+    dxs = block.backward_sweep(xs, gys)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    ws_bwd = torch.cuda.max_memory_allocated() - torch.cuda.memory_allocated()
+    del dxs
+    kt = pkv.pkv_kernel_times()
+    pkv.pkv_kernel_timing(False)
+    attn_ms = sum(kt[k][0] for k in ("select", "fwd", "delta", "dq", "dkdv"))
+    pool_b = block.pool_bytes()
+    block.close()
+    return {"context": n_ctx, "chunk": chunk, "top_k": top_k or None,
+            "forward_sweep_s": round(t1 - t0, 3), "backward_sweep_s": round(t2 - t1, 3),
+            "tokens_per_s": round(n_ctx / (t2 - t0), 1),
+            "attention_kernels_share": round(attn_ms / 1e3 / (t2 - t0), 3),
+            "pool_bytes": pool_b, "pool_bytes_per_token": round(pool_b / n_ctx, 1),
+            "forward_sweep_working_set_bytes": ws_fwd, "backward_sweep_working_set_bytes": ws_bwd}
+
+
 def gemm_peak_tflops(n: int = 8192, reps: int = 20) -> float:
     """bf16 GEMM rate of the box's BLAS (torch.matmul of two contiguous
     n x n bf16 matrices, fp32 accumulate): a measured ceiling for dense bf16
@@ -479,6 +536,11 @@ def main():
     ap.add_argument("--topk-sweep", default="", metavar="K1,K2,..",
                     help="only run the top-K budget sweep on --workload (a top-K workload): "
                          "step time and error against dense attention per budget")
+    ap.add_argument("--block", type=int, default=0, metavar="TOKENS",
+                    help="only run chunk-recurrent training of one Qwen2.5-7B-shaped attention "
+                         "block at TOKENS and TOKENS/2 context (chunks of 12288; --block-top-k K "
+                         "for top-K attention)")
+    ap.add_argument("--block-top-k", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -507,6 +569,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.block:
+        runs = [block_bench(n, 12288, args.block_top_k) for n in (args.block // 2, args.block)]
+        for r in runs:
+            log(f"[bench] block: {r}")
+        print(json.dumps({"metric": "chunk-recurrent attention-block training: tokens/s and memory",
+                          "n_gpus": 1, "dtype": "bf16", "data": "synthetic", "runs": runs}),
+              flush=True)
+        return
     cfg = get_config(args.workload)
     if args.topk_sweep:
         budgets = [int(x) for x in args.topk_sweep.split(",")]

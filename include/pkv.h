@@ -252,6 +252,17 @@ pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
 pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst,
                           hipStream_t stream);
 
+/* The rows [pos0, pos0 + n_tok) of one pool tensor of `layer` in logical
+ * order (copy, never alias): PKV_K, PKV_V -> dst device [n_tok][Hkv][d]
+ * kv_dtype; PKV_DK, PKV_DV -> dst device [n_tok][Hkv][d] fp32.  A
+ * chunk-recurrent backward reads its own chunk's completed dK/dV this way to
+ * carry them back through the K/V projections (sciencestack Figure 3: the
+ * pool's gradients leave the attention outside the autograd graph).  Pools
+ * without a host tier (else PKV_EUNSUPPORTED); the rows must have been
+ * appended (else PKV_EINVAL). */
+pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t pos0,
+                         int64_t n_tok, void* dst, hipStream_t stream);
+
 /* Forget the tokens of `layer` (length back to 0) so that a new sequence can
  * be appended; no memory is freed or cleared (gradients are left as they
  * are: pkv_grad_zero clears them).  Host-only, immediate. */

@@ -27,6 +27,7 @@ EXPORTS = (
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
     "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
     "pkv_kernel_times", "pkv_offload_bytes", "pkv_measure_gather", "pkv_measure_atomics",
+    "pkv_read_rows",
 )
 KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "pkv_read_pages": [P, I32, I32, VP, VP],
             "pkv_pool_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
             "pkv_measure_gather": [P, I32, I64, I64, I32, ctypes.POINTER(pkv_sel), VP, VP],
+            "pkv_read_rows": [P, I32, I32, I64, I64, VP, VP],
             "pkv_measure_atomics": [P, I32, I64, I32, F, VP],
             "pkv_pool_reset": [P, I32],
             "pkv_offload_bytes": [P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
@@ -258,6 +260,12 @@ def pkv_kernel_times() -> dict:
     cnt = (ctypes.c_int64 * n)()
     _check(lib().pkv_kernel_times(n, ms, cnt))
     return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def pkv_read_rows(pool: Pool, layer: int, what: int, pos0: int, dst, stream=None) -> None:
+    """Rows [pos0, pos0 + dst.shape[0]) of K, V, dK or dV of `layer`, logical order."""
+    _check(lib().pkv_read_rows(pool.handle, layer, what, pos0, dst.shape[0], _ptr(dst),
+                               _stream(stream)))
 
 
 def pkv_measure_gather(pool: Pool, layer: int, q_pos0: int, n_q: int, n_q_heads: int, out,

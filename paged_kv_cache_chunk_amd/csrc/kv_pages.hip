@@ -74,7 +74,8 @@ __global__ void __launch_bounds__(1024) reps_kernel(const void* __restrict__ kpo
 // Logical-order export of K / V / dK / dV: dst[t][g][:] = pool[g][slot][t % P][:].
 __global__ void export_rows_kernel(const char* __restrict__ pool, char* __restrict__ dst,
                                    const int32_t* __restrict__ table, int hkv, int page,
-                                   int slots, int max_logical, int row_bytes, int64_t n_tok) {
+                                   int slots, int max_logical, int row_bytes, int64_t t0,
+                                   int64_t n_tok) {
   const int vec_per_row = row_bytes / 16;
   const int64_t total = n_tok * hkv * vec_per_row;
   for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
@@ -82,7 +83,7 @@ __global__ void export_rows_kernel(const char* __restrict__ pool, char* __restri
     const int c = (int)(idx % vec_per_row);
     const int64_t tg = idx / vec_per_row;
     const int g = (int)(tg % hkv);
-    const int64_t t = tg / hkv;
+    const int64_t t = t0 + tg / hkv;
     const int slot = table[(int64_t)g * max_logical + t / page];
     const int64_t src = (((int64_t)g * slots + slot) * page + t % page) * row_bytes + c * 16;
     *reinterpret_cast<uint4*>(dst + tg * row_bytes + c * 16) =
@@ -148,7 +149,7 @@ hipError_t launch_reps(const LayerDev& L, const Geom& g, bool bf16, int64_t firs
 }
 
 hipError_t launch_export(const LayerDev& L, const Geom& g, int what, int elem_bytes,
-                         int64_t n_tok, void* dst, hipStream_t s) {
+                         int64_t n_tok, void* dst, hipStream_t s, int64_t t0) {
   if (n_tok <= 0) return hipSuccess;
   if (what == 4) {
     const int64_t n_pages = (n_tok + g.page - 1) / g.page;
@@ -168,7 +169,7 @@ hipError_t launch_export(const LayerDev& L, const Geom& g, int what, int elem_by
   const int64_t work = n_tok * g.hkv * (row_bytes / 16);
   hipLaunchKernelGGL(export_rows_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s, src,
                      (char*)dst, L.table, g.hkv, g.page, g.slots, g.max_logical, row_bytes,
-                     n_tok);
+                     t0, n_tok);
   return hipGetLastError();
 }
 

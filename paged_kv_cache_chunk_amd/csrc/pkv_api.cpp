@@ -402,6 +402,23 @@ pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst
   return pool_read(pool, layer, what, dst, stream);
 }
 
+pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t pos0,
+                         int64_t n_tok, void* dst, hipStream_t stream) {
+  if (!pool || !dst) return fail(PKV_EINVAL, "pkv_read_rows: null argument");
+  if (layer < 0 || layer >= pool->desc.n_layers)
+    return fail(PKV_EINVAL, "pkv_read_rows: layer %d out of range", layer);
+  if (what < PKV_K || what > PKV_DV) return fail(PKV_EINVAL, "pkv_read_rows: bad `what` %d", what);
+  if (pool->desc.host_tier)
+    return fail(PKV_EUNSUPPORTED, "pkv_read_rows: pools without a host tier only");
+  if (pos0 < 0 || n_tok < 0 || pos0 + n_tok > pool->length[layer])
+    return fail(PKV_EINVAL, "pkv_read_rows: rows [%lld, %lld) outside the %lld appended",
+                (long long)pos0, (long long)(pos0 + n_tok), (long long)pool->length[layer]);
+  hipError_t e = launch_export(layer_view(pool, layer), geom(pool), what, pool->kv_bytes, n_tok,
+                               dst, stream, pos0);
+  if (e != hipSuccess) return hip_fail(e, "pkv_read_rows: launch");
+  return PKV_OK;
+}
+
 pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
                               int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready) {
   if (!pool) return fail(PKV_EINVAL, "pkv_prefetch_pages: null pool");

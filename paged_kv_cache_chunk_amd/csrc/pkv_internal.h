@@ -100,7 +100,7 @@ hipError_t launch_append(const LayerDev& L, const Geom& g, int elem_bytes, int64
 hipError_t launch_reps(const LayerDev& L, const Geom& g, bool bf16, int64_t first_page,
                        int64_t n_pages, int64_t length, hipStream_t s);
 hipError_t launch_export(const LayerDev& L, const Geom& g, int what, int elem_bytes,
-                         int64_t n_tok, void* dst, hipStream_t s);
+                         int64_t n_tok, void* dst, hipStream_t s, int64_t t0 = 0);
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
 
 // ---- kernels in select_topk.hip
