@@ -137,11 +137,15 @@ class LayerBench:
         if warmup == 0:
             self.step(keep_counts=True)
         torch.cuda.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        for _ in range(steps):
+        marks[0].record()
+        for i in range(steps):
             self.step()
+            marks[i + 1].record()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        self.step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
         pkv.pkv_kernel_timing(True)
         for _ in range(steps):
             self.step()
@@ -618,6 +622,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(sorted(lb.step_ms)[len(lb.step_ms) // 2], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
