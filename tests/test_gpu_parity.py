@@ -181,3 +181,35 @@ def test_bf16_other_shapes(hq, hkv, page, sparse_k):
     if sp is not None:
         _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_bf16_topk_covering_every_page_equals_dense(ragged):
+    """A top-K budget at least the number of pages selects, for every query
+    page, all key pages up to its own (in ascending order), so the restricted
+    attention is the full causal one ("Out of the Memory Barrier", section
+    2.D, with the budget covering the context).  The sparse path then visits
+    the same key tiles in the same order as the dense path: O, LSE and dQ must
+    be bit-identical; dK/dV are the same sums, added by atomics in another
+    order."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+
+    n_ctx = 2000 if ragged else 2048
+    cfg = mini_config("qwen_256k_topk", n_ctx=n_ctx, chunk=1024, top_k=16)
+    w = Workload(cfg)
+    dense = run_layer(cfg, w)
+    sparse = run_layer(cfg, w, sparse=Sparse(top_k=cfg.n_pages))
+    for c in range(cfg.n_chunks):
+        pages, count = sparse["sel"][c]
+        q_pos0, n = cfg.chunk_range(c)
+        for il in range(pages.shape[0]):
+            qpage = (q_pos0 + il * cfg.page) // cfg.page
+            for g in range(cfg.hkv):
+                assert list(pages[il, g, :count[il, g]]) == list(range(qpage + 1))
+    for name in ("O", "lse", "dq"):
+        assert np.array_equal(dense[name], sparse[name]), \
+            f"{name}: max diff {np.abs(dense[name] - sparse[name]).max():.3e}"
+    for name in ("dk", "dv"):
+        assert rel_err(sparse[name], dense[name]) <= 1e-5, name
+    dense["pool"].close()
+    sparse["pool"].close()
