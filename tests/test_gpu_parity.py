@@ -213,3 +213,37 @@ def test_bf16_topk_covering_every_page_equals_dense(ragged):
         assert rel_err(sparse[name], dense[name]) <= 1e-5, name
     dense["pool"].close()
     sparse["pool"].close()
+
+
+@pytest.mark.parametrize("sparse_k", [0, 4])
+def test_bf16_chunking_does_not_change_results(sparse_k):
+    """Chunk-recurrent processing gives the results of the whole sequence
+    whatever the (page-aligned) chunk size ("Out of the Memory Barrier",
+    sections 2.A and 2.B): the same sequence cut into chunks of 512, 1024 and
+    2048 rows.  A query row sees the same keys in the same tile order in every
+    cut, so O, LSE and dQ are bit-identical; dK/dV collect the same
+    contributions from a different number of chunks (fp32 atomics, another
+    order).  In top-K mode a query page's selection depends only on its own
+    rows and the keys before it, so the same holds."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    from synthetic.gen import ChunkInputs
+
+    base = mini_config("qwen_256k_topk", n_ctx=2048, chunk=2048, top_k=max(sparse_k, 1))
+    w = Workload(base)
+    f = w.full()  # one sequence, cut three ways below
+    outs = []
+    for chunk in (512, 1024, 2048):
+        cfg = base.replace(chunk=chunk)
+        cuts = [ChunkInputs(p0, f.q[p0:p0 + chunk], f.k[p0:p0 + chunk], f.v[p0:p0 + chunk],
+                            f.do[p0:p0 + chunk]) for p0 in range(0, cfg.n_ctx, chunk)]
+        sp = Sparse(top_k=sparse_k) if sparse_k else None
+        outs.append(run_layer(cfg, w, sparse=sp, table=w.table(), chunks=cuts))
+    ref = outs[-1]
+    for got in outs[:-1]:
+        for name in ("O", "lse", "dq"):
+            assert np.array_equal(got[name], ref[name]), \
+                f"{name}: max diff {np.abs(got[name] - ref[name]).max():.3e}"
+        for name in ("dk", "dv"):
+            assert rel_err(got[name], ref[name]) <= 1e-5, name
+    for o in outs:
+        o["pool"].close()
