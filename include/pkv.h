@@ -117,8 +117,11 @@ typedef struct {
  *          each (query page, KV head), entries past count are ignored;
  *   count  int32 [n_qpages][Hkv].
  * Query page i of a chunk that starts at q_pos0 is absolute page
- * q_pos0 / P + i.  Every list must contain the query page itself and
- * page 0, ascend strictly, and hold only pages <= the query page.
+ * q_pos0 / P + i.  Every list must contain the query page itself (so that
+ * every query sees at least its own key), ascend strictly, and hold only
+ * pages <= the query page; entries outside [0, max_logical_pages) are
+ * clamped into it, so a malformed list cannot make a kernel read outside
+ * the pool (its results are then unspecified).
  */
 typedef struct {
   const int32_t* pages;
@@ -181,7 +184,9 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
  * [n_q][n_q_heads][d] fp32, overwritten) and ADDS dK, dV into the layer's
  * gradient pool with fp32 atomics (dK/dV of a multi-chunk run are the sum
  * of every chunk's contribution).  Uses a library-owned scratch buffer for
- * D = rowsum(dO * O), grown with hipMalloc when a larger chunk arrives.  bf16
+ * D = rowsum(dO * O), the log-sum-exp in base 2 and, with a selection, the
+ * dK/dV work list (the selection inverted per key page); it is grown with
+ * hipMalloc when a larger chunk arrives.  bf16
  * pools run the dQ and dK/dV kernels side by side on a second, library-owned
  * stream forked from and joined back into `stream` with events (capturable
  * into a HIP graph); the call's work is complete, as seen from `stream`, when
