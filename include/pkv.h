@@ -186,7 +186,10 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
  * of every chunk's contribution).  Uses a library-owned scratch buffer for
  * D = rowsum(dO * O), the log-sum-exp in base 2 and, with a selection, the
  * dK/dV work list (the selection inverted per key page); it is grown with
- * hipMalloc when a larger chunk arrives.  bf16
+ * hipMalloc (after a device synchronisation) when a larger chunk arrives.
+ * The scratch is one per pool: backward calls of one pool on different
+ * streams must not overlap.  Chunks of more than 1024 pages are rejected
+ * (PKV_EUNSUPPORTED).  bf16
  * pools run the dQ and dK/dV kernels side by side on a second, library-owned
  * stream forked from and joined back into `stream` with events (capturable
  * into a HIP graph); the call's work is complete, as seen from `stream`, when
@@ -210,7 +213,9 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
  * q is device [n_q][n_q_heads][d] in kv_dtype.  sel_pages is device
  * [ceil(n_q/P)][Hkv][sel_stride] int32 with sel_stride >=
  * top_k + n_sink + n_local (unused entries set to -1); sel_count is device
- * [ceil(n_q/P)][Hkv] int32.  Uses library-owned scratch for the scores. */
+ * [ceil(n_q/P)][Hkv] int32.  Uses library-owned scratch for the scores (one
+ * per pool: selection calls of one pool on different streams must not
+ * overlap).  Contexts beyond 60000 pages are rejected (PKV_EUNSUPPORTED). */
 pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
                                  int32_t n_q_heads, const void* q, int32_t top_k,
                                  int32_t n_sink, int32_t n_local, int32_t* sel_pages,
