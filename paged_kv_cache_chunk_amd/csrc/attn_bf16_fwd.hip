@@ -46,12 +46,12 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   }
 
   int n_tiles;
-  TileWalk<BNT> walk = make_walk<BNT>(c, g, r0, rlast, &n_tiles);
+  TileAhead<BNT> walk = make_ahead<BNT>(c, g, r0, rlast, &n_tiles);
   TileDma<BNT, NW> dma;
   dma.init(w, lane);
-  auto issue = [&](int b, const KeyTile& t) {
-    dma.issue(sm[b], w, key_rows<BNT>(c, c.L.k, g, t), ROWB);
-    dma.issue(sm[b] + TB, w, key_rows<BNT>(c, c.L.v, g, t), ROWB);
+  auto issue = [&](int b, const KeyTile& t, int slot) {
+    dma.issue_direct(sm[b], w, key_rows_at<BNT>(c, c.L.k, g, t, slot), ROWB);
+    dma.issue_direct(sm[b] + TB, w, key_rows_at<BNT>(c, c.L.v, g, t, slot), ROWB);
   };
 
   f32x16 oacc[4][NT];
@@ -67,8 +67,9 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
 
   KeyTile t_cur{0, 0, 0};
   if (n_tiles > 0) {
-    t_cur = walk.next();
-    issue(0, t_cur);
+    int slot;
+    t_cur = walk.take(&slot);
+    issue(0, t_cur, slot);
   }
   wait_dma_and_sync();
 
@@ -76,8 +77,9 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
     const int b = j & 1;
     KeyTile t_next{0, 0, 0};
     if (j + 1 < n_tiles) {
-      t_next = walk.next();
-      issue(b ^ 1, t_next);
+      int slot;
+      t_next = walk.take(&slot);
+      issue(b ^ 1, t_next, slot);
     }
     const char* kt = sm[b];
     const char* vt = sm[b] + TB;

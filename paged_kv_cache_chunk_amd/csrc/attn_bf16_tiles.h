@@ -110,6 +110,42 @@ __device__ __forceinline__ bf16x8 frag_tr(const char* tile, int row0, int col0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Tile copies issued directly (global_load_lds_dwordx4, saddr form: a
+// wave-uniform 64-bit base plus a per-lane 32-bit byte offset; lane l's 16
+// bytes land at lds + 16 l).  The compiler does not see them as LDS writes,
+// so it does not guard later LDS reads of other buffers with waits for them
+// (it cannot tell the buffers apart and would wait for a copy issued for the
+// next tile); the kernels order the copies themselves: s_waitcnt + barrier
+// before a copied buffer is read (wait_dma_and_sync).  M0 holds the LDS
+// address; one wait state separates its write from the copy.  The host pass
+// of the compiler sees no instructions.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(unsigned, (const LDS_AS void*)p);
+#else
+  (void)p;
+  return 0;
+#endif
+}
+__device__ __forceinline__ void copy16(const void* base, unsigned off, unsigned lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // readfirstlane returns int: widen through unsigned, never sign-extend
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const unsigned lu = (unsigned)__builtin_amdgcn_readfirstlane((int)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lu), "v"(off), "s"(bu)
+               : "memory", "m0");
+#else
+  (void)base;
+  (void)off;
+  (void)lds;
+#endif
+}
+
 // Copy R rows of 256 bytes into a swizzled LDS tile with NW waves: one
 // 1 KB global_load_lds per 4 rows; wave w issues instructions w, w + NW, ..
 // Lane l of instruction u moves 16-byte chunk c = ((64 u + l) % 16) ^ swz(row)
@@ -136,6 +172,13 @@ struct TileDma {
       __builtin_amdgcn_global_load_lds((const GLB_AS void*)src,
                                        (LDS_AS void*)(tile + 1024 * (w + x * NW)), 16, 0, 0);
     }
+  }
+  // same, issued directly (copy16); base wave-uniform, offsets non-negative
+  __device__ __forceinline__ void issue_direct(char* tile, int w, const char* base,
+                                               int row_bytes) const {
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+      copy16(base, (unsigned)(row[x] * row_bytes + chunk_b[x]), lds_addr(tile + 1024 * (w + x * NW)));
   }
   // same, with source rows clamped to [0, last_row]
   __device__ __forceinline__ void issue_clamped(char* tile, int w, const char* base, int row_bytes,
@@ -226,6 +269,84 @@ __device__ __forceinline__ TileWalk<BNT> make_walk(const AttnCall& c, int g, int
   }
   *n_tiles = uni(n);
   return W;
+}
+
+// Key tiles in the order of TileWalk, with their page-table lookups done
+// ahead: when tile j is taken (its copy is about to be issued), the slot of
+// tile j+1 has been loaded since the previous take and the list entry of
+// tile j+2 since the one before.  Both lookups are global loads whose
+// results are first used a whole tile later, so their latency overlaps that
+// tile's MFMAs instead of stalling the copy.  Reads past the walk's end stay
+// inside the list and the table (positions and pages are clamped); those
+// tiles are never taken.
+template <int BNT>
+struct TileAhead {
+  const int32_t* list;   // nullptr: dense
+  const int32_t* table;  // page table row of the KV head
+  int tpp, page, max_logical, rel, n_list;
+  int pu, psub;          // walk position of the next list lookup
+  int b_raw, b_sub;      // tile after next: list entry (or page), sub-tile
+  int a_pg, a_sub;       // next tile: page, sub-tile
+  int a_slot;            // its slot (loaded ahead)
+  __device__ __forceinline__ int clamp_pg(int p) const {
+    return p < 0 ? 0 : (p >= max_logical ? max_logical - 1 : p);
+  }
+  __device__ __forceinline__ void lookup_list() {
+    if (list) {
+      const int i = pu < n_list ? pu : n_list - 1;
+      b_raw = list[i < 0 ? 0 : i];
+    } else {
+      b_raw = pu;
+    }
+    b_sub = psub;
+    if (++psub == tpp) {
+      psub = 0;
+      ++pu;
+    }
+  }
+  // the tile after next becomes the next one: its page is known now (the
+  // list entry was loaded a tile ago) and its slot lookup starts; the list
+  // lookup of the following tile starts
+  __device__ __forceinline__ void advance() {
+    a_pg = uni(clamp_pg(b_raw));
+    a_sub = b_sub;
+    a_slot = table[a_pg];
+    lookup_list();
+  }
+  // the next tile, with its slot; then advance
+  __device__ __forceinline__ KeyTile take(int* slot) {
+    KeyTile t{a_pg, a_sub, a_pg * page + a_sub * BNT + rel};
+    *slot = uni(a_slot);
+    advance();
+    return t;
+  }
+};
+
+// The look-ahead walker of a query block (the tiles of make_walk).
+template <int BNT>
+__device__ __forceinline__ TileAhead<BNT> make_ahead(const AttnCall& c, int g, int r0, int rlast,
+                                                     int* n_tiles) {
+  const TileWalk<BNT> W = make_walk<BNT>(c, g, r0, rlast, n_tiles);
+  TileAhead<BNT> A;
+  A.list = W.list;
+  A.table = c.L.table + (int64_t)g * c.g.max_logical;
+  A.tpp = W.tpp;
+  A.page = W.page;
+  A.max_logical = W.max_logical;
+  A.rel = W.rel;
+  A.n_list = W.list ? uni(sel_count(c, r0 / c.g.page, g)) : 0;
+  A.pu = A.psub = 0;
+  A.lookup_list();  // tile 0
+  A.advance();      // tile 0 next (slot loading), tile 1's list entry loading
+  return A;
+}
+
+// Row 0 of key tile t (slot looked up already) of KV head g in `pool`.
+template <int BNT>
+__device__ __forceinline__ const char* key_rows_at(const AttnCall& c, const void* pool, int g,
+                                                   const KeyTile& t, int slot) {
+  return reinterpret_cast<const char*>(pool) +
+         (((int64_t)g * c.g.slots + slot) * c.g.page + t.sub * BNT) * ROWB;
 }
 
 // Row 0 of key tile t of KV head g in `pool`.
