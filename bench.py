@@ -524,7 +524,7 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="qwen_128k_dense")
     ap.add_argument("--sparse-workload", default="qwen_256k_topk",
