@@ -348,7 +348,7 @@ static int dkdv_qpi() {
   static const int q = [] {
     const char* v = getenv("PKV_DKDV_QPI");
     const int x = v ? atoi(v) : 0;
-    return x >= 1 && x <= 1024 ? x : 4;
+    return x >= 1 && x <= 1024 ? x : 2;
   }();
   return q;
 }
