@@ -247,3 +247,67 @@ def test_bf16_chunking_does_not_change_results(sparse_k):
             assert rel_err(got[name], ref[name]) <= 1e-5, name
     for o in outs:
         o["pool"].close()
+
+
+@pytest.mark.parametrize("dtype,sparse_k", [("bf16", 0), ("bf16", 2), ("f32", 0)])
+def test_single_token_context(dtype, sparse_k):
+    """A context of one token.  The only row sees key 0 alone, so its one
+    probability is 1: O is v0 (bit-exact in bf16, where any probability
+    within 2^-9 of 1 rounds back to v0), LSE is the one scaled score, dV is
+    dO summed over the group's query heads, and dQ, dK vanish ("Out of the
+    Memory Barrier", section 2.A: dS = P (dP - D) with dP = D here) up to the
+    rounding of two fp32 sums of the same d products, bounded below by
+    1e-4 of the sum of their magnitudes.  In top-K mode the one query page
+    selects page 0."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    base = "qwen_256k_topk" if sparse_k else "qwen_32k_dense"
+    cfg = mini_config(base, n_ctx=1, chunk=128, top_k=sparse_k).replace(dtype=dtype)
+    sp = Sparse(top_k=sparse_k) if sparse_k else None
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f = w.full()
+    q, k, v, do = (x.astype(np.float64) for x in (f.q, f.k, f.v, f.do))
+    G = cfg.group
+    if sp is not None:
+        pages, count = got["sel"][0]
+        assert count.tolist() == [[1] * cfg.hkv]
+        assert (pages[0, :, 0] == 0).all()
+    for h in range(cfg.hq):
+        g = h // G
+        if dtype == "bf16":
+            assert np.array_equal(got["O"][0, h], v[0, g]), h
+        else:
+            assert rel_err(got["O"][0, h], v[0, g]) <= 1e-6, h
+        s = cfg.scale * float(q[0, h] @ k[0, g])
+        assert abs(got["lse"][h, 0] - s) <= 1e-5 * max(1.0, abs(s)), h
+        mag = cfg.scale * np.abs(do[0, h] * v[0, g]).sum() * np.abs(k[0, g]).max()
+        assert np.abs(got["dq"][0, h]).max() <= 1e-4 * mag, h
+    for g in range(cfg.hkv):
+        heads = range(g * G, (g + 1) * G)
+        assert rel_err(got["dv"][0, g], do[0, g * G:(g + 1) * G].sum(0)) <= TOL[dtype], g
+        mag = cfg.scale * sum(np.abs(do[0, h] * v[0, g]).sum() * np.abs(q[0, h]).max()
+                              for h in heads)
+        assert np.abs(got["dk"][0, g]).max() <= 1e-4 * mag, g
+    got["pool"].close()
+
+
+@pytest.mark.parametrize("name,sparse_k", [("qwen_32k_dense", 0), ("qwen_256k_topk", 3),
+                                           ("tiny_f32", 0)])
+def test_one_token_last_chunk(name, sparse_k):
+    """The last chunk is a single row that opens a new page after full pages:
+    the shortest ragged tail (a one-row query tile, a one-key page and, in
+    top-K mode, a one-row query page whose mean is that row)."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    if name == "tiny_f32":
+        cfg = get_config(name).replace(n_ctx=513)
+    else:
+        cfg = mini_config(name, n_ctx=1025, chunk=512, top_k=sparse_k)
+    assert cfg.chunk_range(cfg.n_chunks - 1)[1] == 1 and (cfg.n_ctx - 1) % cfg.page == 0
+    sp = Sparse(top_k=sparse_k) if sparse_k else None
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f, ref = _oracle_for(cfg, w, sp)
+    if sp is not None:
+        _check_sel(cfg, f, got, ref, sp)
+    _check(cfg, got, ref, TOL[cfg.dtype])
+    got["pool"].close()
