@@ -21,99 +21,93 @@ struct __align__(1024) DkvSmem {
 
 // Work list of the sparse dK/dV kernel (layout in DkvPlan), one workgroup of
 // 1024 threads.  The selection is inverted: for every (KV head g, key page p)
-// the ascending list of the query pages whose selection holds p.  A key page
-// that many query pages selected (the sink pages, pages every query scores
-// high) would otherwise leave one workgroup with all their rows while the
-// rest of the grid idles; here its work is cut into items of at most qpi
-// query pages.  Item order: (g, p, 128-key slab of p, piece).
+// a bit mask of the query pages of the chunk whose selection holds p (bit il
+// % 32 of word il / 32; a page listed twice counts once) and its population
+// count.  A key page that many query pages selected (the sink pages, pages
+// every query scores high) would otherwise leave one workgroup with all their
+// rows while the rest of the grid idles; here its work is cut into items of
+// at most qpi query pages.  Items are ordered by size, largest first, so the
+// workgroups dealt out last are the short ones; an item is (g, 128-key slab,
+// first iteration, end iteration).  Every phase runs over all entries at
+// once: no step is sequential over the query pages.
 __global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, int G, int page,
                                                          int tiles_pp, DkvPlan pl) {
-  __shared__ int s_a[1024], s_b[1024];
+  __shared__ int s_scan[1024];
+  __shared__ int s_next[1025];  // per item size (query pages): item count, then next free index
   const int tid = threadIdx.x;
   int* cnt = pl.base + pl.off_cnt;
-  int* off = pl.base + pl.off_off;
-  int* lst = pl.base + pl.off_lst;
+  unsigned* mask = reinterpret_cast<unsigned*>(pl.base + pl.off_mask);
   int4* items = reinterpret_cast<int4*>(pl.base + pl.off_items);
-  const int E = hkv * pl.n_pages;
+  const int W = pl.mask_words;
+  const int qpi = pl.qpi;
+  const int64_t E = (int64_t)hkv * pl.n_pages;
   const int subs = page / 128;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  for (int64_t x = tid; x < E * W; x += 1024) mask[x] = 0u;
+  for (int q = tid; q <= qpi; q += 1024) s_next[q] = 0;
+  __threadfence();
   __syncthreads();
-  // count (atomics keep the counts exact even if a list names a page twice)
+  // mark: every (query page, KV head, list entry) in parallel, atomics at L2
   const int per_qp = hkv * sel.stride;
-  for (int il = 0; il < sel.n_qpages; ++il) {
-    for (int x = tid; x < per_qp; x += 1024) {
-      const int g = x / sel.stride, j = x % sel.stride;
-      int n = sel.count[(int64_t)il * hkv + g];
-      n = n < 0 ? 0 : (n > sel.stride ? sel.stride : n);
-      if (j < n) {
-        const int p = sel.pages[((int64_t)il * hkv + g) * sel.stride + j];
-        if (p >= 0 && p < pl.n_pages) atomicAdd(&cnt[g * pl.n_pages + p], 1);
-      }
+  const int64_t n_ent = (int64_t)sel.n_qpages * per_qp;
+  for (int64_t x = tid; x < n_ent; x += 1024) {
+    const int il = (int)(x / per_qp);
+    const int r = (int)(x % per_qp);
+    const int g = r / sel.stride, j = r % sel.stride;
+    int n = sel.count[(int64_t)il * hkv + g];
+    n = n < 0 ? 0 : (n > sel.stride ? sel.stride : n);
+    if (j < n && il < 32 * W) {
+      const int p = sel.pages[((int64_t)il * hkv + g) * sel.stride + j];
+      if (p >= 0 && p < pl.n_pages)
+        atomicOr(&mask[((int64_t)g * pl.n_pages + p) * W + (il >> 5)], 1u << (il & 31));
     }
-    __syncthreads();
   }
-  // exclusive scans of list lengths and item counts; thread t owns a
-  // contiguous run of entries
-  const int run = (E + 1023) / 1024;
-  const int e0 = tid * run < E ? tid * run : E;
-  const int e1 = e0 + run < E ? e0 + run : E;
-  auto n_items = [&](int c) { return c > 0 ? subs * ((c + pl.qpi - 1) / pl.qpi) : 0; };
-  // the counters were updated by atomics (at L2): read them past the L1
-  auto count_of = [&](int e) { return __hip_atomic_load(&cnt[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  int sa = 0, sb = 0;
-  for (int e = e0; e < e1; ++e) {
-    const int cv = count_of(e);
-    sa += cv;
-    sb += n_items(cv);
-  }
-  s_a[tid] = sa;
-  s_b[tid] = sb;
+  __threadfence();
   __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
-    const int va = tid >= d ? s_a[tid - d] : 0;
-    const int vb = tid >= d ? s_b[tid - d] : 0;
+  // counts and item counts per size; thread t owns a contiguous run of
+  // entries.  The masks were written by atomics (at L2): read past the L1.
+  const int64_t run = (E + 1023) / 1024;
+  const int64_t e0 = tid * run < E ? tid * run : E;
+  const int64_t e1 = e0 + run < E ? e0 + run : E;
+  for (int64_t e = e0; e < e1; ++e) {
+    int cv = 0;
+    for (int w = 0; w < W; ++w)
+      cv += __popc(__hip_atomic_load(&mask[e * W + w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    cnt[e] = cv;
+    if (cv > 0) {
+      if (cv >= qpi) atomicAdd(&s_next[qpi], (cv / qpi) * subs);
+      if (cv % qpi) atomicAdd(&s_next[cv % qpi], subs);
+    }
+  }
+  __syncthreads();
+  // first index of each size, largest size first: inclusive scan over
+  // t = qpi - size (Hillis-Steele)
+  const int hv = tid < qpi ? s_next[qpi - tid] : 0;
+  s_scan[tid] = hv;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? s_scan[tid - d] : 0;
     __syncthreads();
-    s_a[tid] += va;
-    s_b[tid] += vb;
+    s_scan[tid] += v;
     __syncthreads();
   }
-  int oa = s_a[tid] - sa, ob = s_b[tid] - sb;
-  const int total_items = s_b[1023] < pl.max_items ? s_b[1023] : pl.max_items;
-  for (int e = e0; e < e1; ++e) {
-    const int cv = count_of(e);
-    off[e] = oa;
-    oa += cv;
+  if (tid < qpi) s_next[qpi - tid] = s_scan[tid] - hv;
+  if (tid == 0) pl.base[0] = s_scan[1023] < pl.max_items ? s_scan[1023] : pl.max_items;
+  __syncthreads();
+  for (int64_t e = e0; e < e1; ++e) {
+    const int cv = cnt[e];  // written by this thread above
     if (cv == 0) continue;
-    const int g = e / pl.n_pages, p = e % pl.n_pages;
-    const int it_total = cv * tiles_pp * G;
-    const int it_step = pl.qpi * tiles_pp * G;
-    for (int sub = 0; sub < subs; ++sub)
-      for (int i0 = 0; i0 < it_total; i0 += it_step) {
-        const int i1 = i0 + it_step < it_total ? i0 + it_step : it_total;
-        if (ob < pl.max_items) items[ob] = make_int4(g, p * subs + sub, i0, i1);
-        ++ob;
-      }
-  }
-  if (tid == 0) pl.base[0] = total_items;
-  __syncthreads();  // every thread has read its counts before they are reset
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;  // reused as fill cursors
-  __syncthreads();
-  // fill one query page at a time, so every list is ascending; each entry
-  // receives exactly as many writes as it was counted, inside its own range
-  for (int il = 0; il < sel.n_qpages; ++il) {
-    for (int x = tid; x < per_qp; x += 1024) {
-      const int g = x / sel.stride, j = x % sel.stride;
-      int n = sel.count[(int64_t)il * hkv + g];
-      n = n < 0 ? 0 : (n > sel.stride ? sel.stride : n);
-      if (j < n) {
-        const int p = sel.pages[((int64_t)il * hkv + g) * sel.stride + j];
-        if (p >= 0 && p < pl.n_pages) {
-          const int e = g * pl.n_pages + p;
-          lst[off[e] + atomicAdd(&cnt[e], 1)] = il;
-        }
+    const int g = (int)(e / pl.n_pages), p = (int)(e % pl.n_pages);
+    const int per_page = tiles_pp * G;  // iterations per query page
+    const int it_total = cv * per_page;
+    const int it_step = qpi * per_page;
+    for (int i0 = 0; i0 < it_total; i0 += it_step) {
+      const int i1 = i0 + it_step < it_total ? i0 + it_step : it_total;
+      const int size = (i1 - i0) / per_page;
+      for (int sub = 0; sub < subs; ++sub) {
+        const int b = atomicAdd(&s_next[size], 1);
+        if (b < pl.max_items) items[b] = make_int4(g, p * subs + sub, i0, i1);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -151,10 +145,25 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
         it0 < 0)
       return;  // not a valid item (cannot happen for a plan written by dkdv_plan_kernel)
     const int e = g * c.plan.n_pages + (int)((int64_t)slab * 128 / P);
+    const int W = c.plan.mask_words;  // <= 32 (chunks of at most 1024 pages)
     int n = uni(pb[c.plan.off_cnt + e]);
-    n = n < 1024 ? n : 1024;  // at most one hit per query page
-    const int* lst = pb + c.plan.off_lst + pb[c.plan.off_off + e];
-    for (int i = tid; i < n; i += 256) sm.qpl[i] = lst[i];
+    n = n < 32 * W ? n : 32 * W;
+    // the query pages of the mask, ascending: lane t < W expands word t after
+    // the population counts of the words before it
+    if (w == 0) {
+      const unsigned* mw = reinterpret_cast<const unsigned*>(pb + c.plan.off_mask) + (int64_t)e * W;
+      unsigned bits = lane < W ? mw[lane] : 0u;
+      int pos = __popc(bits);
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(pos, d);
+        if (lane >= d) pos += v;
+      }
+      pos -= __popc(bits);
+      while (bits) {
+        sm.qpl[pos++] = 32 * lane + __ffs(bits) - 1;
+        bits &= bits - 1;
+      }
+    }
     __syncthreads();
     n_rt = n * tiles_pp;
     if (it1 > n_rt * G) it1 = n_rt * G;
@@ -348,7 +357,7 @@ static int dkdv_qpi() {
   static const int q = [] {
     const char* v = getenv("PKV_DKDV_QPI");
     const int x = v ? atoi(v) : 0;
-    return x >= 1 && x <= 1024 ? x : 2;
+    return x >= 1 && x <= 1024 ? x : 8;
   }();
   return q;
 }
@@ -360,13 +369,12 @@ DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel
   pl.n_pages = (int)((n_keys + g.page - 1) / g.page);
   pl.qpi = dkdv_qpi();
   const int64_t nqp = (n_q + g.page - 1) / g.page;
+  pl.mask_words = (int)((nqp + 31) / 32);
   const int64_t E = (int64_t)g.hkv * pl.n_pages;
-  pl.lst_cap = nqp * g.hkv * (sel_stride > 0 ? sel_stride : 0);
+  const int64_t H = nqp * g.hkv * (sel_stride > 0 ? sel_stride : 0);  // list entries
   pl.off_cnt = 64;
-  pl.off_off = pl.off_cnt + E;
-  pl.off_lst = pl.off_off + E;
-  pl.off_items = ((pl.off_lst + pl.lst_cap + 3) / 4) * 4;
-  const int64_t H = pl.lst_cap;
+  pl.off_mask = pl.off_cnt + E;
+  pl.off_items = ((pl.off_mask + E * pl.mask_words + 3) / 4) * 4;
   const int64_t bound = (H + pl.qpi - 1) / pl.qpi + (H < E ? H : E);
   pl.max_items = (int)((H < bound ? H : bound) * (g.page / 128));
   pl.bytes = (pl.off_items + 4 * (int64_t)pl.max_items) * 4;

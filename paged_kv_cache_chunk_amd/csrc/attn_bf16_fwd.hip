@@ -85,78 +85,101 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
     const char* vt = sm[b] + TB;
     const int srel0 = t_cur.srel0;  // tile's first key, relative to q_pos0
     if (srel0 <= tw_max) {
+      // S^T = K Q^T for this tile; keys past a row get -inf on tiles that
+      // cross this wave's causal diagonal
       f32x16 sacc[MT][NT];
+      auto scores = [&]() {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
+          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 a = frag_row(kt, 32 * mt + l32, ks, half);
+          for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 a = frag_row(kt, 32 * mt + l32, ks, half);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma(a, qf[nt][ks], sacc[mt][nt]);
+            for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma(a, qf[nt][ks], sacc[mt][nt]);
+          }
         }
-      }
-      if (srel0 + BNT - 1 > tw_min) {  // tile crosses the causal diagonal of this wave
+        if (srel0 + BNT - 1 > tw_min) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int sr = srel0 + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (sr > t_rel[nt]) sacc[mt][nt][r] = -INFINITY;
-            }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-        // Lazy rescale: keep the reference maximum unless a row's maximum
-        // grew by more than 2^8 (probabilities stay <= 256, exact enough in
-        // fp32 and representable in bf16).
-        if (__any(mx > m_ref[nt] + 8.f)) {
-          const float mr = fmaxf(m_ref[nt], mx);
-          const float alpha = ex2(m_ref[nt] - mr);
-          l_i[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) oacc[dt][nt] *= alpha;
-          m_ref[nt] = mr;
+              for (int r = 0; r < 16; ++r) {
+                const int sr = srel0 + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (sr > t_rel[nt]) sacc[mt][nt][r] = -INFINITY;
+              }
         }
+      };
+      // Probabilities 2^(s c2 - m_ref) of column tile nt, packed to bf16 in
+      // MFMA B-operand order (pk[kk] = rows 16 kk .. 16 kk + 15 of the tile);
+      // returns their sum, taken over the packed values (v_dot2c with ones),
+      // i.e. over exactly the weights the P V product uses.
+      u32x4 pk[2 * MT][NT];
+      auto probs = [&](int nt) -> float {
         const float mneg = -m_ref[nt];
         float rs = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int kk = 0; kk < 2 * MT; ++kk) {
+          const int mt = kk >> 1, rb = 8 * (kk & 1);
+          float p[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = ex2(fmaf(sacc[mt][nt][r], c2, mneg));
-            sacc[mt][nt][r] = p;
-            rs += p;
-          }
+          for (int e = 0; e < 8; ++e) p[e] = ex2(fmaf(sacc[mt][nt][rb + e], c2, mneg));
+          u32x4 v;
+          v.x = pack2(p[0], p[1]);
+          v.y = pack2(p[2], p[3]);
+          v.z = pack2(p[4], p[5]);
+          v.w = pack2(p[6], p[7]);
+          pk[kk][nt] = v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rs = dot2_ones(v[e], rs);
+        }
+        return rs;
+      };
+      scores();
+      // Lazy rescale: the reference maximum m_ref is kept while every
+      // probability stays <= 2^8 (exact enough in fp32, representable in
+      // bf16).  The probabilities are computed against it; if a row's sum
+      // over the tile exceeds 2^8 (which any probability above 2^8 implies;
+      // also inf or NaN, as on a wave's first tile, where m_ref = -inf), the
+      // reference moves to the running row maximum, O and l are rescaled and
+      // the probabilities are computed again.  On i.i.d. scores the first
+      // tile's maximum is rarely exceeded by 8 (base 2), so the per-tile
+      // maximum search is skipped on almost every tile.
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float rs, alpha = 1.f;
+        bool moved = false;
+#pragma nounroll
+        for (int pass = 0;; ++pass) {
+          rs = probs(nt);
+          if (pass == 1 || !__any(!(rs <= 256.f))) break;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mt][nt][r]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+          const float mr = fmaxf(m_ref[nt], mx);
+          alpha = ex2(m_ref[nt] - mr);
+          m_ref[nt] = mr;
+          moved = true;
+        }
+        if (moved) {
+          l_i[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt][nt] *= alpha;
+        }
         l_i[nt] += rs;
       }
 #pragma unroll
       for (int kk = 0; kk < 2 * MT; ++kk) {
-        bf16x8 pf[NT];
-        const int mt = kk >> 1, rb = 8 * (kk & 1);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          u32x4 pv;
-          pv.x = pack2(sacc[mt][nt][rb + 0], sacc[mt][nt][rb + 1]);
-          pv.y = pack2(sacc[mt][nt][rb + 2], sacc[mt][nt][rb + 3]);
-          pv.z = pack2(sacc[mt][nt][rb + 4], sacc[mt][nt][rb + 5]);
-          pv.w = pack2(sacc[mt][nt][rb + 6], sacc[mt][nt][rb + 7]);
-          pf[nt] = as_bf16x8(pv);
-        }
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const bf16x8 a = frag_tr(vt, 16 * kk, 32 * dt, lane);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma(a, pf[nt], oacc[dt][nt]);
+          for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma(a, as_bf16x8(pk[kk][nt]), oacc[dt][nt]);
         }
       }
     }

@@ -83,6 +83,13 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
+// acc + (sum of the two bf16 values packed in w), one v_dot2c_f32_bf16 with
+// (1, 1): the products are exact, the sum is taken in fp32.
+__device__ __forceinline__ float dot2_ones(unsigned w, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+}
+
 // Raw v_exp_f32 (2^x); arguments are <= 8 or -inf here.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 

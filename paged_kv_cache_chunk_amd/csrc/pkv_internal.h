@@ -45,10 +45,10 @@ struct SelDev {
 //   items[max_items]     int4 {g, 128-key slab, first, end iteration}
 struct DkvPlan {
   int* base;
-  int n_pages;  // key pages of the chunk's context
-  int qpi;      // query pages per work item
-  int64_t off_cnt, off_off, off_lst, off_items;
-  int64_t lst_cap;
+  int n_pages;     // key pages of the chunk's context
+  int qpi;         // query pages per work item (at most 1024)
+  int mask_words;  // 32-bit words per (KV head, key page) query-page mask
+  int64_t off_cnt, off_mask, off_items;
   int max_items;
   int64_t bytes;
 };
