@@ -44,12 +44,18 @@ class GpuWorkload:
         return torch.randn(shape, generator=g, device=self.device, dtype=torch.float32)
 
     def _rope(self, x: torch.Tensor, pos0: int) -> torch.Tensor:
+        # angles computed on the device (fp64): no host-to-device copy, which
+        # from pageable memory would synchronise the host with the device
+        # (and, on the default stream, with every other stream) in the middle
+        # of a timed sweep
         n, _, d = x.shape
         half = d // 2
-        inv = self.cfg.rope_base ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
-        ang = np.arange(pos0, pos0 + n, dtype=np.float64)[:, None] * inv[None, :]
-        c = torch.from_numpy(np.cos(ang).astype(np.float32)).to(self.device)[:, None, :]
-        s = torch.from_numpy(np.sin(ang).astype(np.float32)).to(self.device)[:, None, :]
+        dev = x.device
+        inv = float(self.cfg.rope_base) ** (
+            -torch.arange(half, dtype=torch.float64, device=dev) * 2.0 / d)
+        ang = torch.arange(pos0, pos0 + n, dtype=torch.float64, device=dev)[:, None] * inv[None, :]
+        c = torch.cos(ang).to(torch.float32)[:, None, :]
+        s = torch.sin(ang).to(torch.float32)[:, None, :]
         x1, x2 = x[..., :half], x[..., half:]
         return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
 
