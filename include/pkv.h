@@ -234,6 +234,17 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
 pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
                               int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready);
 
+/* Host-tier pools only (PKV_OK and no work otherwise): as pkv_prefetch_pages
+ * for a dense chunk whose last query is key n_keys - 1: brings the pages of
+ * keys 0 .. n_keys - 1 of `layer` (and with_grads != 0: their dK/dV), the
+ * only pages causal attention of that chunk reads or whose gradients it
+ * changes (de 2.C: prefetch of the next layer's KV; the chunk attends to
+ * every earlier page plus its own, de 2.A).  pkv_writeback_grads then writes
+ * back the same pages.  1 <= n_keys <= the layer's appended length, else
+ * PKV_EINVAL. */
+pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t with_grads,
+                               hipStream_t copy_stream, hipEvent_t ready);
+
 /* Host-tier pools only: write the dK/dV pages of `layer` that the last
  * prefetch with grads brought in back to host memory (fp32 -> host gradient
  * dtype) on copy_stream, after the attention calls on `layer` issued so far

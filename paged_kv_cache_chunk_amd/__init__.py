@@ -27,7 +27,7 @@ EXPORTS = (
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
     "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
     "pkv_kernel_times", "pkv_offload_bytes", "pkv_measure_gather", "pkv_measure_atomics",
-    "pkv_read_rows",
+    "pkv_read_rows", "pkv_prefetch_prefix",
 )
 KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
                              ctypes.POINTER(pkv_sel), VP, VP],
             "pkv_select_topk_pages": [P, I32, I64, I64, I32, VP, I32, I32, I32, VP, VP, I32, VP],
             "pkv_prefetch_pages": [P, I32, ctypes.POINTER(pkv_sel), I32, VP, VP],
+            "pkv_prefetch_prefix": [P, I32, I64, I32, VP, VP],
             "pkv_writeback_grads": [P, I32, VP, VP],
             "pkv_grad_zero": [P, I32, VP],
             "pkv_read_pages": [P, I32, I32, VP, VP],
@@ -217,6 +218,13 @@ def pkv_prefetch_pages(pool: Pool, layer: int, sel=None, with_grads: bool = Fals
     ev = None if ready is None else ready.cuda_event
     _check(lib().pkv_prefetch_pages(pool.handle, layer, _selp(sel), int(with_grads),
                                     _stream(copy_stream), ev))
+
+
+def pkv_prefetch_prefix(pool: Pool, layer: int, n_keys: int, with_grads: bool = False,
+                        copy_stream=None, ready=None) -> None:
+    ev = None if ready is None else ready.cuda_event
+    _check(lib().pkv_prefetch_prefix(pool.handle, layer, n_keys, int(with_grads),
+                                     _stream(copy_stream), ev))
 
 
 def pkv_writeback_grads(pool: Pool, layer: int, copy_stream=None, done=None) -> None:

@@ -98,19 +98,30 @@ class OffloadSweep:
                               stream=self.compute)
         return sel
 
+    def _prefetch(self, layer: int, ch: dict, sel):
+        """The layer's pages for this chunk, with their gradients: the
+        selected pages (top-K), or the pages of keys 0 .. the chunk's last
+        query (dense; later pages are neither read nor changed)."""
+        from . import pkv_prefetch_pages, pkv_prefetch_prefix
+        if sel is None:
+            pkv_prefetch_prefix(self.pool, layer, ch["q_pos0"] + ch["q"].shape[0], with_grads=True,
+                                copy_stream=self.copy)
+        else:
+            pkv_prefetch_pages(self.pool, layer, sel, with_grads=True, copy_stream=self.copy)
+
     def chunk(self, c: int, inputs, bufs, outputs=None):
         """Backward-sweep step of chunk c over every layer.  bufs[layer]:
         ChunkBuffers sized for this chunk (two alternating sets suffice).
         outputs(layer, c, buf) is called after the layer's backward is
         enqueued (on the compute stream) to collect results."""
-        from . import pkv_prefetch_pages, pkv_writeback_grads
+        from . import pkv_writeback_grads
         L = self.L
         ins = {L - 1: inputs(L - 1, c)}
         sel = self._select(L - 1, ins[L - 1], bufs[L - 1])
         ev = torch.cuda.Event()
         ev.record(self.compute)
         self.copy.wait_event(ev)
-        pkv_prefetch_pages(self.pool, L - 1, sel, with_grads=True, copy_stream=self.copy)
+        self._prefetch(L - 1, ins[L - 1], sel)
         for layer in range(L - 1, -1, -1):
             if layer - 1 >= 0:
                 ins[layer - 1] = inputs(layer - 1, c)
@@ -118,8 +129,7 @@ class OffloadSweep:
                 ev = torch.cuda.Event()
                 ev.record(self.compute)
                 self.copy.wait_event(ev)
-                pkv_prefetch_pages(self.pool, layer - 1, nsel, with_grads=True,
-                                   copy_stream=self.copy)
+                self._prefetch(layer - 1, ins[layer - 1], nsel)
             ch, b = ins.pop(layer), bufs[layer]
             pkv_attn_fwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, b.lse, self.scale,
                          sel=b.sel, stream=self.compute)

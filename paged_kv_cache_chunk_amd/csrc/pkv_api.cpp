@@ -430,7 +430,22 @@ pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
   }
   if (sel && (!sel->pages || !sel->count || sel->stride < 1 || sel->n_qpages < 0))
     return fail(PKV_EINVAL, "pkv_prefetch_pages: malformed selection");
-  return pool_prefetch(pool, layer, sel, with_grads != 0, copy_stream, ready);
+  return pool_prefetch(pool, layer, sel, 0, with_grads != 0, copy_stream, ready);
+}
+
+pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t with_grads,
+                               hipStream_t copy_stream, hipEvent_t ready) {
+  if (!pool) return fail(PKV_EINVAL, "pkv_prefetch_prefix: null pool");
+  if (layer < 0 || layer >= pool->desc.n_layers)
+    return fail(PKV_EINVAL, "pkv_prefetch_prefix: layer %d out of range", layer);
+  if (n_keys < 1 || n_keys > pool->length[layer])
+    return fail(PKV_EINVAL, "pkv_prefetch_prefix: n_keys=%lld outside [1, %lld appended]",
+                (long long)n_keys, (long long)pool->length[layer]);
+  if (!pool->desc.host_tier) {
+    if (ready) PKV_HIP(hipEventRecord(ready, copy_stream), "pkv_prefetch_prefix: hipEventRecord");
+    return PKV_OK;
+  }
+  return pool_prefetch(pool, layer, nullptr, n_keys, with_grads != 0, copy_stream, ready);
 }
 
 pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written) {

@@ -223,7 +223,7 @@ pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s) {
   return PKV_OK;
 }
 
-pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_grads,
+pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_keys, bool with_grads,
                          hipStream_t cs, hipEvent_t ready) {
   const int w = p->window_of(layer);
   const pkv_pool_desc& d = p->desc;
@@ -237,7 +237,9 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_g
       return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
   }
   uint8_t* need = p->d_need + (int64_t)w * d.n_kv_heads * d.max_logical_pages;
-  const int64_t n_pages = (p->length[layer] + d.page_size - 1) / d.page_size;
+  // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every appended key)
+  const int64_t n_avail = n_keys > 0 && n_keys < p->length[layer] ? n_keys : p->length[layer];
+  const int64_t n_pages = (n_avail + d.page_size - 1) / d.page_size;
   if ((e = launch_need_clear(need, (int64_t)d.n_kv_heads * d.max_logical_pages, cs)) != hipSuccess ||
       (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");

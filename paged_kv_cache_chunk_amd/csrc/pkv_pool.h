@@ -70,7 +70,7 @@ pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s);
 pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s);
-pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, bool with_grads,
+pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_keys, bool with_grads,
                          hipStream_t copy_stream, hipEvent_t ready);
 pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t copy_stream, hipEvent_t done);
 pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written);

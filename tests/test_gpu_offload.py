@@ -26,7 +26,7 @@ CFG = mini_config("qwen_1m_offload", n_ctx=4096, chunk=1024, n_layers=3, top_k=6
                   slots=32)
 
 
-def _sweep(cfg, host_tier, host_grad_dtype=None):
+def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True):
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -48,7 +48,7 @@ def _sweep(cfg, host_tier, host_grad_dtype=None):
         for l in range(L):
             ch = chunks[(l, c)]
             pkv.pkv_append_kv(pool, l, ch.q_pos0, dev(ch.k), dev(ch.v))
-    sp = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local)
+    sp = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local) if sparse else None
     sweep = OffloadSweep(pool, L, cfg.hq, cfg.hkv, cfg.d, cfg.page, cfg.scale, sp, torch.bfloat16)
     got = {}
 
@@ -58,7 +58,7 @@ def _sweep(cfg, host_tier, host_grad_dtype=None):
 
     def outputs(l, c, b):
         got[(l, c)] = dict(O=b.o.float().cpu(), lse=b.lse.cpu(), dq=b.dq.cpu(),
-                           sel=(b.sel[0].cpu(), b.sel[1].cpu()))
+                           sel=(b.sel[0].cpu(), b.sel[1].cpu()) if sparse else None)
 
     for c in reversed(range(cfg.n_chunks)):
         bufs = {l: ChunkBuffers(chunks[(l, c)].n_q, cfg.hq, cfg.hkv, cfg.d, cfg.page,
@@ -113,6 +113,49 @@ def test_offloaded_matches_resident_and_oracle():
         print(f"layer {l}: dK/dV error, bf16 host grads {e_off:.2e}, all-HBM fp32 {e_res:.2e}",
               flush=True)
         assert e_off < 1e-2 and e_res < 1e-2
+
+
+def test_offloaded_dense_matches_resident_and_oracle():
+    """Dense chunks prefetch only the pages of keys up to their last query
+    (pkv_prefetch_prefix) and write back the same pages' gradients."""
+    cfg = CFG.replace(n_layers=2)
+    off, goff, _, _ = _sweep(cfg, True, sparse=False)
+    res, gres, _, _ = _sweep(cfg, False, sparse=False)
+    for key in res:
+        for name in ("O", "lse", "dq"):
+            assert np.array_equal(off[key][name].numpy(), res[key][name].numpy()), (key, name)
+    for l in range(cfg.n_layers):
+        f = Workload(cfg, layer=l).full()
+        ref = oracle.run_chunks(f.q, f.k, f.v, f.do, cfg.chunk, cfg.scale, cfg.page)
+        for c in range(cfg.n_chunks):
+            q_pos0, n = cfg.chunk_range(c)
+            sl = slice(q_pos0, q_pos0 + n)
+            assert rel_err(off[(l, c)]["O"].numpy(), ref["O"][sl]) < 1e-2
+            assert rel_err(off[(l, c)]["dq"].numpy(), ref["dq"][sl]) < 1e-2
+        e_off = max(rel_err(goff[l][0], ref["dk"]), rel_err(goff[l][1], ref["dv"]))
+        e_res = max(rel_err(gres[l][0], ref["dk"]), rel_err(gres[l][1], ref["dv"]))
+        print(f"dense layer {l}: dK/dV error, bf16 host grads {e_off:.2e}, all-HBM fp32 {e_res:.2e}",
+              flush=True)
+        assert e_off < 1e-2 and e_res < 1e-2
+
+
+def test_prefetch_prefix_arguments():
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    cfg = CFG.replace(n_layers=2)
+    pool = pkv.pkv_pool_create(2, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
+                               pkv.PKV_BF16, host_tier=1)
+    k = torch.zeros(256, cfg.hkv, cfg.d, dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_append_kv(pool, 0, 0, k, k)
+    for bad in (0, 257):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_prefetch_prefix(pool, 0, bad)
+        assert e.value.status == 1  # PKV_EINVAL
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_prefetch_prefix(pool, 2, 1)
+    pkv.pkv_prefetch_prefix(pool, 0, 256, with_grads=True)
+    torch.cuda.synchronize()
+    pool.close()
 
 
 def test_offloaded_fp32_grad_tier_matches_resident():
