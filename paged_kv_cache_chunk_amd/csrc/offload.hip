@@ -40,18 +40,20 @@ __global__ void need_mark_all_kernel(uint8_t* need, int max_logical, int64_t n_p
   if (j < n_pages) need[(int64_t)blockIdx.y * max_logical + j] = 1;
 }
 
-// Copies `bytes` (a multiple of 4 KiB) with every thread keeping 4 16-byte
-// loads in flight (host-mapped sources are slow to answer).
+// Copies `bytes` (a multiple of 4 KiB) with every thread keeping kInflight
+// 16-byte loads in flight (host-mapped sources answer after microseconds, so
+// a workgroup's bandwidth is its bytes in flight over that latency).
+constexpr int kInflight = 8;
 __device__ __forceinline__ void copy_bytes(char* __restrict__ dst, const char* __restrict__ src,
                                            int64_t bytes) {
   const int64_t step = (int64_t)blockDim.x * 16;
-  for (int64_t i = threadIdx.x * 16; i < bytes; i += 4 * step) {
-    uint4 v[4];
+  for (int64_t i = threadIdx.x * 16; i < bytes; i += kInflight * step) {
+    uint4 v[kInflight];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kInflight; ++u)
       if (i + u * step < bytes) v[u] = *reinterpret_cast<const uint4*>(src + i + u * step);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kInflight; ++u)
       if (i + u * step < bytes) *reinterpret_cast<uint4*>(dst + i + u * step) = v[u];
   }
 }
@@ -65,23 +67,23 @@ __device__ __forceinline__ float4 hi4(uint4 a) {
                      __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xffff0000u));
 }
 
-// bf16 [n] -> fp32 [n], n a multiple of 8 * blockDim * 2.
+// bf16 [n] -> fp32 [n], n a multiple of 8 * blockDim; kInflight 16-byte
+// loads in flight per thread.
 __device__ __forceinline__ void widen(float* __restrict__ dst, const unsigned short* __restrict__ src,
                                       int64_t n) {
   const int64_t n8 = n / 8;
-  for (int64_t i = threadIdx.x; i < n8; i += 2 * (int64_t)blockDim.x) {
-    const uint4 a = reinterpret_cast<const uint4*>(src)[i];
-    const bool two = i + blockDim.x < n8;
-    uint4 b = a;
-    if (two) b = reinterpret_cast<const uint4*>(src)[i + blockDim.x];
-    float4* d = reinterpret_cast<float4*>(dst + 8 * i);
-    d[0] = lo4(a);
-    d[1] = hi4(a);
-    if (two) {
-      float4* e = reinterpret_cast<float4*>(dst + 8 * (i + blockDim.x));
-      e[0] = lo4(b);
-      e[1] = hi4(b);
-    }
+  for (int64_t i = threadIdx.x; i < n8; i += kInflight * (int64_t)blockDim.x) {
+    uint4 a[kInflight];
+#pragma unroll
+    for (int u = 0; u < kInflight; ++u)
+      if (i + u * blockDim.x < n8) a[u] = reinterpret_cast<const uint4*>(src)[i + u * blockDim.x];
+#pragma unroll
+    for (int u = 0; u < kInflight; ++u)
+      if (i + u * blockDim.x < n8) {
+        float4* d = reinterpret_cast<float4*>(dst + 8 * (i + u * blockDim.x));
+        d[0] = lo4(a[u]);
+        d[1] = hi4(a[u]);
+      }
   }
 }
 
