@@ -27,11 +27,15 @@ struct __align__(1024) DkvSmem {
 // every query scores high) would otherwise leave one workgroup with all their
 // rows while the rest of the grid idles; here its work is cut into items of
 // at most qpi query pages.  Items are ordered by size, largest first, so the
-// workgroups dealt out last are the short ones; an item is (g, 128-key slab,
-// first iteration, end iteration).  Every phase runs over all entries at
-// once: no step is sequential over the query pages.
+// workgroups dealt out last are the short ones.  An item is two int4: (g,
+// 128-key slab, first iteration, end iteration) and (page-table slot of the
+// slab's page, number of query pages, mask words 0 and 1), so that a
+// workgroup has everything it needs after one round of loads when the chunk
+// has at most 64 query pages.  Every phase runs over all entries at once: no
+// step is sequential over the query pages.
 __global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, int G, int page,
-                                                         int tiles_pp, DkvPlan pl) {
+                                                         int tiles_pp, const int32_t* table,
+                                                         int max_logical, DkvPlan pl) {
   __shared__ int s_scan[1024];
   __shared__ int s_next[1025];  // per item size (query pages): item count, then next free index
   const int tid = threadIdx.x;
@@ -97,6 +101,9 @@ __global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, in
     const int cv = cnt[e];  // written by this thread above
     if (cv == 0) continue;
     const int g = (int)(e / pl.n_pages), p = (int)(e % pl.n_pages);
+    const int slot = table[(int64_t)g * max_logical + p];
+    const int m0 = (int)__hip_atomic_load(&mask[e * W], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int m1 = W > 1 ? (int)__hip_atomic_load(&mask[e * W + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     const int per_page = tiles_pp * G;  // iterations per query page
     const int it_total = cv * per_page;
     const int it_step = qpi * per_page;
@@ -105,7 +112,10 @@ __global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, in
       const int size = (i1 - i0) / per_page;
       for (int sub = 0; sub < subs; ++sub) {
         const int b = atomicAdd(&s_next[size], 1);
-        if (b < pl.max_items) items[b] = make_int4(g, p * subs + sub, i0, i1);
+        if (b < pl.max_items) {
+          items[2 * (int64_t)b] = make_int4(g, p * subs + sub, i0, i1);
+          items[2 * (int64_t)b + 1] = make_int4(slot, cv, m0, m1);
+        }
       }
     }
   }
@@ -132,27 +142,35 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   // This workgroup's KV head, 128-key slab and range [it0, it1) of its
   // iterations; iteration it = head (it / n_rt) x row tile (it % n_rt) over the
   // n_rt row tiles (BQT query rows) of the chunk that can see the slab.
-  int g, slab, it0, it1, n_rt, r_first = 0;
+  int g, slab, it0, it1, n_rt, r_first = 0, slot = 0;
   if (c.sel.pages) {
+    // the item's two int4 (bid is below the grid, the list's capacity) and the
+    // item count, loaded together
     const int* pb = c.plan.base;
+    const int4* rec = reinterpret_cast<const int4*>(pb + c.plan.off_items) + 2 * (int64_t)bid;
+    const int4 r0 = rec[0], r1 = rec[1];
     if (bid >= pb[0]) return;
-    const int4 item = reinterpret_cast<const int4*>(pb + c.plan.off_items)[bid];
-    g = uni(item.x);
-    slab = uni(item.y);
-    it0 = uni(item.z);
-    it1 = uni(item.w);
+    g = uni(r0.x);
+    slab = uni(r0.y);
+    it0 = uni(r0.z);
+    it1 = uni(r0.w);
+    slot = uni(r1.x);
     if (g < 0 || g >= c.g.hkv || slab < 0 || (int64_t)slab * 128 >= (int64_t)c.plan.n_pages * P ||
-        it0 < 0)
+        it0 < 0 || slot < 0 || slot >= c.g.slots)
       return;  // not a valid item (cannot happen for a plan written by dkdv_plan_kernel)
-    const int e = g * c.plan.n_pages + (int)((int64_t)slab * 128 / P);
     const int W = c.plan.mask_words;  // <= 32 (chunks of at most 1024 pages)
-    int n = uni(pb[c.plan.off_cnt + e]);
+    int n = uni(r1.y);
     n = n < 32 * W ? n : 32 * W;
     // the query pages of the mask, ascending: lane t < W expands word t after
-    // the population counts of the words before it
+    // the population counts of the words before it (words 0 and 1 come with
+    // the item)
     if (w == 0) {
-      const unsigned* mw = reinterpret_cast<const unsigned*>(pb + c.plan.off_mask) + (int64_t)e * W;
-      unsigned bits = lane < W ? mw[lane] : 0u;
+      unsigned bits = lane == 0 ? (unsigned)r1.z : (lane == 1 && W > 1 ? (unsigned)r1.w : 0u);
+      if (W > 2) {
+        const int e = g * c.plan.n_pages + (int)((int64_t)slab * 128 / P);
+        const unsigned* mw = reinterpret_cast<const unsigned*>(pb + c.plan.off_mask) + (int64_t)e * W;
+        if (lane >= 2 && lane < W) bits = mw[lane];
+      }
       int pos = __popc(bits);
       for (int d = 1; d < 64; d <<= 1) {
         const int v = __shfl_up(pos, d);
@@ -187,7 +205,7 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
   const int s_rel = (int)(wk0 + l32 - c.q_pos0);  // this lane's key, relative to q_pos0
 
   bf16x8 kf[8], vf[8];
-  const int slot = uni(c.L.table[(int64_t)g * c.g.max_logical + kpage]);
+  if (!c.sel.pages) slot = uni(c.L.table[(int64_t)g * c.g.max_logical + kpage]);
   const int64_t prow = ((int64_t)g * c.g.slots + slot) * P + ((wk0 + l32) % P);
   {
     const u16* kr = reinterpret_cast<const u16*>(c.L.k) + prow * D + 8 * half;
@@ -377,7 +395,7 @@ DkvPlan dkdv_plan_layout(const Geom& g, int hq, int64_t q_pos0, int n_q, int sel
   pl.off_items = ((pl.off_mask + E * pl.mask_words + 3) / 4) * 4;
   const int64_t bound = (H + pl.qpi - 1) / pl.qpi + (H < E ? H : E);
   pl.max_items = (int)((H < bound ? H : bound) * (g.page / 128));
-  pl.bytes = (pl.off_items + 4 * (int64_t)pl.max_items) * 4;
+  pl.bytes = (pl.off_items + 8 * (int64_t)pl.max_items) * 4;
   return pl;
 }
 
@@ -422,7 +440,7 @@ static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s) {
   if (c.sel.pages) {
     if (c.plan.max_items == 0) return hipSuccess;  // nothing selected
     hipLaunchKernelGGL(dkdv_plan_kernel, dim3(1), dim3(1024), 0, s, c.sel, c.g.hkv, G, c.g.page,
-                       c.g.page / (rows32 ? 32 : 64), c.plan);
+                       c.g.page / (rows32 ? 32 : 64), c.L.table, c.g.max_logical, c.plan);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     grid = dim3(c.plan.max_items);
   } else {

@@ -40,9 +40,9 @@ struct SelDev {
 // kernel from the selection (int32 words at base):
 //   [0]                  number of work items
 //   cnt  [hkv][n_pages]  query pages whose selection holds key page p (head g)
-//   off  [hkv][n_pages]  start of that ascending query-page list in lst
-//   lst  [lst_cap]
-//   items[max_items]     int4 {g, 128-key slab, first, end iteration}
+//   mask [hkv][n_pages][mask_words]  those query pages as a bit mask
+//   items[max_items]     two int4 each: {g, 128-key slab, first, end iteration}
+//                        and {slot of the slab's page, query pages, mask words 0, 1}
 struct DkvPlan {
   int* base;
   int n_pages;     // key pages of the chunk's context
