@@ -137,7 +137,7 @@ def test_f32_partial_page_tail():
     _check(cfg, got, ref, TOL["f32"])
 
 
-@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 4)])
+@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 4), (2, 1)])
 def test_bf16_local_window_mode(n_sink, n_local):
     """top_k = 0: the selection is the forced pages only (sink pages and a
     window of the n_local most recent pages), i.e. sliding-window attention
