@@ -14,7 +14,7 @@ Headline: 128K-token dense context (chunks of 12288, pages of 128); the
 4096) is reported in the same line.  FLOPs use the algorithmic count
 14 * d * Hq per attended (query, key) pair (4 d forward + 10 d backward).
 
-Prints ONE JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -563,7 +563,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(no multi-GPU path in this build)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
