@@ -529,7 +529,7 @@ def main():
     ap.add_argument("--workload", default="qwen_128k_dense")
     ap.add_argument("--sparse-workload", default="qwen_256k_topk",
                     help="second workload in the same line ('none' to skip)")
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=384,
                     help="query rows in the oracle's CPU sample (0 skips it)")
     ap.add_argument("--layers", type=int, default=0,
                     help="offloaded workload: number of layers (default: the config's)")
