@@ -183,6 +183,22 @@ def test_bf16_other_shapes(hq, hkv, page, sparse_k):
     _check(cfg, got, ref, TOL["bf16"])
 
 
+def test_bf16_sparse_chunk_over_64_query_pages():
+    """A top-K chunk of 71 query pages: the sparse dK/dV work items carry the
+    first two 32-bit words of their key page's query-page mask and the kernel
+    reads the third from the plan (chunks of more than 64 query pages); the
+    sink page, held by every query page, is cut into items of 8."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    n_ctx = 70 * 128 + 40
+    cfg = mini_config("qwen_256k_topk", n_ctx=n_ctx, chunk=n_ctx, hq=4, hkv=1, top_k=3)
+    sp = Sparse(top_k=3)
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    f, ref = _oracle_for(cfg, w, sp)
+    _check_sel(cfg, f, got, ref, sp)
+    _check(cfg, got, ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("ragged", [False, True])
 def test_bf16_topk_covering_every_page_equals_dense(ragged):
     """A top-K budget at least the number of pages selects, for every query
