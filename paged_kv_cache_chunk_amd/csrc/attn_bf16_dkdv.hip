@@ -361,15 +361,6 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
 
 }  // namespace
 
-// PKV_DKDV: "1x32" / "1x64" (32- or 64-row query tiles)
-static bool dkdv_rows32() {
-  static const bool r = [] {
-    const char* v = getenv("PKV_DKDV");
-    return v && !strcmp(v, "1x32");
-  }();
-  return r;
-}
-
 // Query pages per work item of the sparse dK/dV kernel (PKV_DKDV_QPI overrides).
 static int dkdv_qpi() {
   static const int q = [] {
@@ -432,7 +423,7 @@ hipError_t launch_bwd_bf16(const AttnCall& c, hipStream_t s, hipStream_t aux, hi
 
 static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s) {
   hipError_t e = hipSuccess;
-  const bool rows32 = dkdv_rows32();
+  constexpr int kBQT = 64;  // query rows per dK/dV tile
   const int G = c.hq / c.g.hkv;
   int splits = 1;
   dim3 grid;
@@ -440,7 +431,7 @@ static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s) {
   if (c.sel.pages) {
     if (c.plan.max_items == 0) return hipSuccess;  // nothing selected
     hipLaunchKernelGGL(dkdv_plan_kernel, dim3(1), dim3(1024), 0, s, c.sel, c.g.hkv, G, c.g.page,
-                       c.g.page / (rows32 ? 32 : 64), c.L.table, c.g.max_logical, c.plan);
+                       c.g.page / kBQT, c.L.table, c.g.max_logical, c.plan);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     grid = dim3(c.plan.max_items);
   } else {
@@ -451,10 +442,7 @@ static hipError_t launch_dkdv(const AttnCall& c, hipStream_t s) {
     if (splits > 16) splits = 16;
     grid = dim3(n_slabs * c.g.hkv * splits);
   }
-  if (rows32)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<1, 32>), grid, dim3(256), 0, s, c, splits);
-  else
-    hipLaunchKernelGGL((dkdv_bf16_kernel<1, 64>), grid, dim3(256), 0, s, c, splits);
+  hipLaunchKernelGGL((dkdv_bf16_kernel<1, kBQT>), grid, dim3(256), 0, s, c, splits);
   return hipGetLastError();
 }
 

@@ -175,18 +175,8 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
 
 hipError_t launch_dq_bf16(const AttnCall& c, hipStream_t s) {
   const int nqb = (c.n_q + BM - 1) / BM;
-  static const int choice = tile_choice("PKV_DQ_TILE", 0);
   KernelTimer t(KT_DQ, s);
-  switch (choice) {
-    case 1:
-      hipLaunchKernelGGL((dq_bf16_kernel<2, 32>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
-      break;
-    case 2:
-      hipLaunchKernelGGL((dq_bf16_kernel<2, 64>), dim3(nqb * c.hq), dim3(128), 0, s, c, nqb);
-      break;
-    default:
-      hipLaunchKernelGGL((dq_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
-  }
+  hipLaunchKernelGGL((dq_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
   return hipGetLastError();
 }
 

@@ -370,17 +370,5 @@ __device__ __forceinline__ void wait_dma_and_sync() {
   __syncthreads();
 }
 
-// Tile shape of the forward and dQ kernels: NT x 32 query rows per wave,
-// BNT keys per LDS tile.  PKV_FWD_TILE / PKV_DQ_TILE ("1x64", "2x32", "2x64")
-// override the defaults for tuning.
-inline int tile_choice(const char* env, int dflt) {
-  const char* v = getenv(env);
-  if (!v) return dflt;
-  if (!strcmp(v, "1x64")) return 0;
-  if (!strcmp(v, "2x32")) return 1;
-  if (!strcmp(v, "2x64")) return 2;
-  return dflt;
-}
-
 }  // namespace
 }  // namespace pkv
