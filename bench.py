@@ -394,14 +394,16 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
+def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) -> dict:
     """Host-offloaded stack: every layer's K/V and KV-gradient pools in pinned
     host memory (bf16), an HBM window of two layers, the next layer's
     selected pages prefetched on a side stream during the current layer, and
     gradient pages written back asynchronously.  Times the backward sweep
     (chunks last to first, layers last to first: select + prefetch + forward
     + backward + writeback); the forward sweep that appends every chunk's
-    K/V to the host tier is untimed setup."""
+    K/V to the host tier is untimed setup.  host_accumulate: the window's
+    gradients start at zero and the library's host threads add each visit's
+    contributions into the host tier (no gradient bytes host -> HBM)."""
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -416,7 +418,8 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
         t0 = time.time()
         pool = pkv.pkv_pool_create(L, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
                                    pkv.PKV_BF16, host_tier=host_tier, host_grad_dtype=pkv.PKV_BF16,
-                                   device_budget_bytes=cfg.hbm_cap_bytes if host_tier else 0)
+                                   device_budget_bytes=cfg.hbm_cap_bytes if host_tier else 0,
+                                   host_grad_accumulate=host_accumulate if host_tier else 0)
         dev_b, host_b = pkv.pkv_pool_bytes(pool)
         for l in range(L):
             tab = ws[l].table()
@@ -462,6 +465,7 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
                     f"{len(chunk_ids)}, {time.perf_counter() - t0:.1f}s, "
                     f"fetched {fb / 1e9:.1f} GB, written back {wb / 1e9:.1f} GB")
         torch.cuda.synchronize()
+        pkv.pkv_offload_bytes(pool)  # returns after the pending host gradient adds
         wall = time.perf_counter() - t0
         kt = pkv.pkv_kernel_times()
         pkv.pkv_kernel_timing(False)
@@ -491,7 +495,10 @@ def offload_bench(cfg, steps: int, resident_ab: bool) -> dict:
         "workload": f"{cfg.name}: {L} layers, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, "
                     + (f"top-K {cfg.top_k} + {cfg.n_sink} sink + {cfg.n_local} local pages"
                        if cfg.sparse else "dense causal")
-                    + ", K/V and gradient pools in pinned host memory (bf16), HBM window of 2 layers",
+                    + ", K/V and gradient pools in pinned host memory (bf16), HBM window of 2 layers"
+                    + (", gradient contributions added on the host" if host_accumulate else
+                       ", gradients accumulated in HBM"),
+        "host_grad_accumulate": host_accumulate,
         "chunks_timed": off["chunks"],
         "tokens_per_s_per_layer": round(tokens * L / off["wall_s"], 1),
         "backward_sweep_s": round(off["wall_s"], 3),
@@ -535,6 +542,9 @@ def main():
                     help="offloaded workload: number of layers (default: the config's)")
     ap.add_argument("--chunks", type=int, default=0,
                     help="offloaded workload: time only the last N chunks of the backward sweep")
+    ap.add_argument("--host-accumulate", type=int, default=0, choices=(0, 1),
+                    help="offloaded workload: add gradient contributions on the host instead of "
+                         "fetching the gradients into HBM")
     ap.add_argument("--resident-ab", action="store_true",
                     help="offloaded workload: also run the same sweep with all pools in HBM")
     ap.add_argument("--topk-sweep", default="", metavar="K1,K2,..",
@@ -592,7 +602,7 @@ def main():
     if cfg.host_tier:
         if args.layers:
             cfg = cfg.replace(n_layers=args.layers)
-        res = offload_bench(cfg, args.chunks, args.resident_ab)
+        res = offload_bench(cfg, args.chunks, args.resident_ab, args.host_accumulate)
         res.update({"metric": f"offloaded {'top-K' if cfg.sparse else 'dense'} stack: "
                               "backward-sweep tokens/s per layer",
                     "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic"})

@@ -93,6 +93,23 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *                pkv_prefetch_pages fills; representatives and page tables
  *                stay in HBM.
  *   host_grad_dtype  host-tier gradient storage (PKV_F32 or PKV_BF16).
+ *   host_grad_accumulate  host-tier only (else PKV_EINVAL).  0: a prefetch
+ *                with grads brings the pages' accumulated dK/dV into HBM
+ *                and pkv_writeback_grads writes the sums back.  1: the
+ *                window's gradient pages start at zero on every prefetch
+ *                with grads (nothing is read from the host for them),
+ *                pkv_writeback_grads stages only that visit's contributions
+ *                (in host_grad_dtype) in pinned memory, and threads of the
+ *                library add them into the host tier.  The host link then
+ *                carries K/V one way and contributions the other, instead
+ *                of K/V + gradients one way and gradients the other.  Costs
+ *                pinned staging of two layers' dK/dV (host_grad_dtype) and,
+ *                with bf16 host gradients, one more bf16 rounding per visit
+ *                (contribution and sum are both rounded).  The adds finish
+ *                asynchronously; every call that reads or zeroes the host
+ *                gradients waits for them.  Thread count: environment
+ *                variable PKV_HOST_ADD_THREADS, else min(16, CPUs the
+ *                process may run on).
  *   device_budget_bytes  host-tier only: cap on the library's HBM use; pool
  *                creation fails with PKV_ENOMEM if the window does not fit
  *                (0 = no cap).
@@ -107,7 +124,7 @@ typedef struct {
   int32_t kv_dtype;        /* pkv_dtype */
   int32_t host_tier;       /* 0 or 1 */
   int32_t host_grad_dtype; /* pkv_dtype, host-tier only */
-  int32_t reserved;
+  int32_t host_grad_accumulate; /* 0 or 1, host-tier only */
   int64_t device_budget_bytes;
 } pkv_pool_desc;
 
@@ -248,18 +265,24 @@ pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, in
 /* Host-tier pools only: write the dK/dV pages of `layer` that the last
  * prefetch with grads brought in back to host memory (fp32 -> host gradient
  * dtype) on copy_stream, after the attention calls on `layer` issued so far
- * have finished.  `done`, if not NULL, is recorded when the copies finish. */
+ * have finished.  `done`, if not NULL, is recorded when the copies finish.
+ * With host_grad_accumulate the copies go to the window's pinned staging,
+ * `done` means they are staged, and the library's host threads then add
+ * them into the host tier; the call first waits (on the host) until the adds
+ * of the window's previous writeback have finished, since they read the
+ * same staging, and a second writeback of one prefetch is PKV_ESTATE (it
+ * would add the same contributions twice). */
 pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_stream,
                                hipEvent_t done);
 
 /* Host-tier pools: total bytes moved so far by pkv_prefetch_pages (host ->
  * HBM, K/V and gradients) and by pkv_writeback_grads (HBM -> host), counted
- * on the device by the copy kernels.  Synchronises the device.  Both are 0
- * without a host tier. */
+ * on the device by the copy kernels.  Synchronises the device and waits
+ * for pending host gradient adds.  Both are 0 without a host tier. */
 pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written);
 
 /* Zero the dK/dV pool of `layer` (all slots; the host tier too in host-tier
- * mode, synchronously). */
+ * mode, synchronously, after any pending host adds). */
 pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
 
 /* Export (copy, never alias) pool contents of `layer` in logical order, for
@@ -269,7 +292,7 @@ pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
  *   PKV_REPS       -> dst device [n_pages][Hkv][d] fp32;
  * where n_tok = pkv_length(layer) and n_pages = ceil(n_tok / P).  In
  * host-tier mode K/V/dK/dV are read from the host tier (synchronises the
- * device first). */
+ * device first, and waits for pending host adds). */
 pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst,
                           hipStream_t stream);
 

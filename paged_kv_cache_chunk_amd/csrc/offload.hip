@@ -6,10 +6,12 @@
 // nl, "Methodologie", asynchronous CPU offloading; de 2.D: page-level
 // sparsity also shrinks the offload traffic, because only the selected pages
 // move).  The union of the pages a selection names is marked in a per-window
-// byte map; one workgroup per (page, KV head) then copies that page-head if
-// marked.  Gradients travel as the host gradient dtype and live in HBM as
-// fp32 while the layer computes.  Two device counters add up the bytes
-// fetched and written back.
+// byte map, which one small kernel turns into a list of page-heads; the copy
+// kernels stream over that list.  Gradients travel as the host gradient dtype and live in HBM as
+// fp32 while the layer computes; with host accumulation they are not
+// fetched but zeroed in the window, and the writeback sends the window's
+// contributions to a pinned staging area instead of the tier.  Two device
+// counters add up the bytes fetched and written back.
 #include "pkv_pool.h"
 
 namespace pkv {
@@ -40,10 +42,58 @@ __global__ void need_mark_all_kernel(uint8_t* need, int max_logical, int64_t n_p
   if (j < n_pages) need[(int64_t)blockIdx.y * max_logical + j] = 1;
 }
 
-// Copies `bytes` (a multiple of 4 KiB) with every thread keeping kInflight
-// 16-byte loads in flight (host-mapped sources answer after microseconds, so
-// a workgroup's bandwidth is its bytes in flight over that latency).
+// The marked page-heads of a window as a dense list of element offsets
+// (page-major, then KV head), and its length: one workgroup, a block scan
+// over the map.  The copy kernels then stream over the list without
+// touching the map or the page table again.
+__global__ void __launch_bounds__(1024) need_compact_kernel(
+    const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
+    int slots, int hkv, int n_pages, int64_t page_elems, int64_t* __restrict__ items,
+    int* __restrict__ count) {
+  __shared__ int s_sum[1024];
+  const int64_t n = (int64_t)n_pages * hkv;
+  const int tid = threadIdx.x, T = blockDim.x;
+  const int64_t per = (n + T - 1) / T;
+  const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
+  int c = 0;
+  for (int64_t i = lo; i < hi; ++i) c += need[(i % hkv) * max_logical + i / hkv] != 0;
+  s_sum[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < T; off <<= 1) {
+    const int add = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += add;
+    __syncthreads();
+  }
+  int pos = s_sum[tid] - c;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int64_t at = (i % hkv) * max_logical + i / hkv;
+    if (need[at]) items[pos++] = ((i % hkv) * slots + table[at]) * page_elems;
+  }
+  if (tid == T - 1) *count = s_sum[T - 1];
+}
+
+__device__ __forceinline__ float4 lo4(uint4 a) {
+  return make_float4(__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xffff0000u),
+                     __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xffff0000u));
+}
+__device__ __forceinline__ float4 hi4(uint4 a) {
+  return make_float4(__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xffff0000u),
+                     __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xffff0000u));
+}
+
+// A small persistent grid (kCopyBlocks workgroups) does the host-link copies,
+// so that they occupy a few CUs next to the attention kernels instead of
+// flooding the whole GPU.  Each workgroup copies whole page-heads from the
+// list (its next list entry loaded one page-head ahead).  Host-mapped memory
+// answers after microseconds, so a workgroup's bandwidth is its bytes in
+// flight over that latency: every thread keeps kInflight 16-byte loads in
+// flight.  (A flat stream of 16-byte units over all listed page-heads was
+// slower on the host link: 38 vs 42 GB/s host -> HBM, 41 vs 50 back.)
+constexpr int kCopyBlocks = 24;
 constexpr int kInflight = 8;
+
+// Copies `bytes` (a multiple of 16 * blockDim).
 __device__ __forceinline__ void copy_bytes(char* __restrict__ dst, const char* __restrict__ src,
                                            int64_t bytes) {
   const int64_t step = (int64_t)blockDim.x * 16;
@@ -58,17 +108,7 @@ __device__ __forceinline__ void copy_bytes(char* __restrict__ dst, const char* _
   }
 }
 
-__device__ __forceinline__ float4 lo4(uint4 a) {
-  return make_float4(__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xffff0000u),
-                     __uint_as_float(a.y << 16), __uint_as_float(a.y & 0xffff0000u));
-}
-__device__ __forceinline__ float4 hi4(uint4 a) {
-  return make_float4(__uint_as_float(a.z << 16), __uint_as_float(a.z & 0xffff0000u),
-                     __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xffff0000u));
-}
-
-// bf16 [n] -> fp32 [n], n a multiple of 8 * blockDim; kInflight 16-byte
-// loads in flight per thread.
+// bf16 [n] -> fp32 [n], n a multiple of 8 * blockDim.
 __device__ __forceinline__ void widen(float* __restrict__ dst, const unsigned short* __restrict__ src,
                                       int64_t n) {
   const int64_t n8 = n / 8;
@@ -87,77 +127,92 @@ __device__ __forceinline__ void widen(float* __restrict__ dst, const unsigned sh
   }
 }
 
-// Work items are (page, KV head) pairs; a small persistent grid (kCopyBlocks
-// workgroups) walks them so that the copies occupy a few CUs next to the
-// attention kernels instead of flooding the whole GPU.
-constexpr int kCopyBlocks = 24;
-
+// Host -> window for every listed page-head: K and V (with_kv), and dK/dV
+// with grad_mode 1 (bf16 host gradients, widened to fp32) or 2 (fp32).
 __global__ void __launch_bounds__(256) fetch_kernel(
-    const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
-    int slots, int hkv, int n_pages, int64_t page_elems, int kv_bytes,
-    const char* __restrict__ hk, const char* __restrict__ hv, char* __restrict__ wk,
-    char* __restrict__ wv, bool with_grads, bool grad_bf16, const void* __restrict__ hdk,
-    const void* __restrict__ hdv, float* __restrict__ wdk, float* __restrict__ wdv,
+    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    bool with_kv, int kv_bytes, const char* __restrict__ hk, const char* __restrict__ hv,
+    char* __restrict__ wk, char* __restrict__ wv, int grad_mode, const char* __restrict__ hdk,
+    const char* __restrict__ hdv, float* __restrict__ wdk, float* __restrict__ wdv,
     unsigned long long* __restrict__ moved) {
-  unsigned long long mine = 0;
-  for (int item = blockIdx.x; item < n_pages * hkv; item += gridDim.x) {
-    const int g = item % hkv, j = item / hkv;
-    if (!need[(int64_t)g * max_logical + j]) continue;
-    const int slot = table[(int64_t)g * max_logical + j];
-    const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
-    copy_bytes(wk + e0 * kv_bytes, hk + e0 * kv_bytes, page_elems * kv_bytes);
-    copy_bytes(wv + e0 * kv_bytes, hv + e0 * kv_bytes, page_elems * kv_bytes);
-    mine += 2 * page_elems * kv_bytes;
-    if (!with_grads) continue;
-    if (!grad_bf16) {
-      copy_bytes((char*)(wdk + e0), (const char*)hdk + e0 * 4, page_elems * 4);
-      copy_bytes((char*)(wdv + e0), (const char*)hdv + e0 * 4, page_elems * 4);
-      mine += 2 * page_elems * 4;
-    } else {
+  const int n = *count;
+  const int64_t per = (with_kv ? 2 * page_elems * kv_bytes : 0) +
+                      (grad_mode ? 2 * page_elems * (grad_mode == 1 ? 2 : 4) : 0);
+  int it = blockIdx.x;
+  int64_t e0 = it < n ? items[it] : 0;
+  for (; it < n; it += gridDim.x) {
+    const int64_t e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : 0;
+    if (with_kv) {
+      copy_bytes(wk + e0 * kv_bytes, hk + e0 * kv_bytes, page_elems * kv_bytes);
+      copy_bytes(wv + e0 * kv_bytes, hv + e0 * kv_bytes, page_elems * kv_bytes);
+    }
+    if (grad_mode == 1) {
       widen(wdk + e0, (const unsigned short*)hdk + e0, page_elems);
       widen(wdv + e0, (const unsigned short*)hdv + e0, page_elems);
-      mine += 2 * page_elems * 2;
+    } else if (grad_mode == 2) {
+      copy_bytes((char*)(wdk + e0), hdk + e0 * 4, page_elems * 4);
+      copy_bytes((char*)(wdv + e0), hdv + e0 * 4, page_elems * 4);
     }
+    e0 = e_next;
   }
-  if (threadIdx.x == 0 && mine) atomicAdd(moved, mine);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n) atomicAdd(moved, (unsigned long long)n * per);
+}
+
+// Zero the window's fp32 dK/dV of every listed page-head (host gradient
+// accumulation: each visit starts from zero).  HBM-only work, so a full grid
+// rather than the copy kernels' small one, which keeps the host link's
+// workgroups on host reads.
+__global__ void __launch_bounds__(256) window_grad_zero_kernel(
+    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    float* __restrict__ wdk, float* __restrict__ wdv) {
+  const int64_t per = page_elems / 4;  // float4 per page-head
+  const int64_t total = (int64_t)*count * per;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t it = u / per, e = items[it] + (u - it * per) * 4;
+    *reinterpret_cast<float4*>(wdk + e) = z;
+    *reinterpret_cast<float4*>(wdv + e) = z;
+  }
 }
 
 __device__ __forceinline__ unsigned to_bf16(float x) {
   return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
-// window fp32 grads -> host gradient dtype, same persistent walk.
+// Window fp32 dK/dV of the listed page-heads -> host gradient dtype (the
+// tier, or the staging of host accumulation, indexed alike), whole
+// page-heads per workgroup as in the fetch.
 __global__ void __launch_bounds__(256) writeback_kernel(
-    const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
-    int slots, int hkv, int n_pages, int64_t page_elems, bool grad_bf16, void* __restrict__ hdk,
-    void* __restrict__ hdv, const float* __restrict__ wdk, const float* __restrict__ wdv,
+    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    bool grad_bf16, char* __restrict__ hdk, char* __restrict__ hdv,
+    const float* __restrict__ wdk, const float* __restrict__ wdv,
     unsigned long long* __restrict__ moved) {
-  unsigned long long mine = 0;
-  for (int item = blockIdx.x; item < n_pages * hkv; item += gridDim.x) {
-    const int g = item % hkv, j = item / hkv;
-    if (!need[(int64_t)g * max_logical + j]) continue;
-    const int slot = table[(int64_t)g * max_logical + j];
-    const int64_t e0 = ((int64_t)g * slots + slot) * page_elems;
+  const int n = *count;
+  int it = blockIdx.x;
+  int64_t e0 = it < n ? items[it] : 0;
+  for (; it < n; it += gridDim.x) {
+    const int64_t e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : 0;
     if (!grad_bf16) {
-      copy_bytes((char*)hdk + e0 * 4, (const char*)(wdk + e0), page_elems * 4);
-      copy_bytes((char*)hdv + e0 * 4, (const char*)(wdv + e0), page_elems * 4);
-      mine += 2 * page_elems * 4;
-      continue;
+      copy_bytes(hdk + e0 * 4, (const char*)(wdk + e0), page_elems * 4);
+      copy_bytes(hdv + e0 * 4, (const char*)(wdv + e0), page_elems * 4);
+    } else {
+      uint4* dk = reinterpret_cast<uint4*>(hdk + e0 * 2);
+      uint4* dv = reinterpret_cast<uint4*>(hdv + e0 * 2);
+      for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
+        const float4* a = reinterpret_cast<const float4*>(wdk + e0 + 8 * i);
+        const float4* b = reinterpret_cast<const float4*>(wdv + e0 + 8 * i);
+        const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+        dk[i] = make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
+                           to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
+        dv[i] = make_uint4(to_bf16(b0.x) | (to_bf16(b0.y) << 16), to_bf16(b0.z) | (to_bf16(b0.w) << 16),
+                           to_bf16(b1.x) | (to_bf16(b1.y) << 16), to_bf16(b1.z) | (to_bf16(b1.w) << 16));
+      }
     }
-    uint4* dk = reinterpret_cast<uint4*>((unsigned short*)hdk + e0);
-    uint4* dv = reinterpret_cast<uint4*>((unsigned short*)hdv + e0);
-    for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
-      const float4* a = reinterpret_cast<const float4*>(wdk + e0 + 8 * i);
-      const float4* b = reinterpret_cast<const float4*>(wdv + e0 + 8 * i);
-      const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-      dk[i] = make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
-                         to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
-      dv[i] = make_uint4(to_bf16(b0.x) | (to_bf16(b0.y) << 16), to_bf16(b0.z) | (to_bf16(b0.w) << 16),
-                         to_bf16(b1.x) | (to_bf16(b1.y) << 16), to_bf16(b1.z) | (to_bf16(b1.w) << 16));
-    }
-    mine += 2 * page_elems * 2;
+    e0 = e_next;
   }
-  if (threadIdx.x == 0 && mine) atomicAdd(moved, mine);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n)
+    atomicAdd(moved, (unsigned long long)n * 2 * page_elems * (grad_bf16 ? 2 : 4));
 }
 
 // dst[t][g][:] (fp32) = bf16 host gradient of token t
@@ -205,38 +260,86 @@ hipError_t launch_need_mark(uint8_t* need, const pkv_sel* sel, int hkv, int max_
   return hipGetLastError();
 }
 
-hipError_t launch_fetch_pages(const pkv_pool* p, int layer, int window, bool with_grads,
-                              hipStream_t s) {
+int64_t need_words(const pkv_pool* p) {
+  return (int64_t)p->desc.n_kv_heads * p->desc.max_logical_pages;
+}
+
+namespace {
+
+struct WindowList {
+  const uint8_t* need;
+  int64_t* items;
+  int* count;
+};
+
+// The page map and list buffer the window's last prefetch built.
+WindowList window_list(const pkv_pool* p, int window) {
+  const int64_t nw = need_words(p);
+  const int b = window * 2 + p->list_gen[window];
+  return {p->d_need + b * nw, p->d_items + b * nw, p->d_count + b};
+}
+
+int64_t pages_of(const pkv_pool* p, int layer) {
+  return (p->length[layer] + p->desc.page_size - 1) / p->desc.page_size;
+}
+
+}  // namespace
+
+hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStream_t s) {
   const pkv_pool_desc& d = p->desc;
-  const int64_t n_pages = (p->length[layer] + d.page_size - 1) / d.page_size;
-  if (n_pages <= 0) return hipSuccess;
-  const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
-  const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
-  const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
+  const WindowList L = window_list(p, window);
+  const int32_t* table = p->d_table + (int64_t)layer * need_words(p);
+  hipLaunchKernelGGL(need_compact_kernel, dim3(1), dim3(1024), 0, s, L.need, table,
+                     d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)pages_of(p, layer),
+                     (int64_t)d.page_size * d.head_dim, L.items, L.count);
+  return hipGetLastError();
+}
+
+hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s) {
+  if (pages_of(p, layer) <= 0) return hipSuccess;
+  const pkv_pool_desc& d = p->desc;
+  const WindowList L = window_list(p, window);
   KernelTimer t(KT_FETCH, s);
-  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, need,
-                     table, d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)n_pages, page_elems,
-                     p->kv_bytes,
+  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
+                     (int64_t)d.page_size * d.head_dim, true, p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
                      (char*)p->d_k + window * p->layer_elems * p->kv_bytes,
-                     (char*)p->d_v + window * p->layer_elems * p->kv_bytes, with_grads,
-                     d.host_grad_dtype == PKV_BF16, (const void*)p->m_dk[layer],
-                     (const void*)p->m_dv[layer], p->d_dk + window * p->layer_elems,
-                     p->d_dv + window * p->layer_elems, p->d_moved);
+                     (char*)p->d_v + window * p->layer_elems * p->kv_bytes, 0, nullptr, nullptr,
+                     nullptr, nullptr, p->d_moved);
+  return hipGetLastError();
+}
+
+hipError_t launch_fetch_grads(const pkv_pool* p, int layer, int window, hipStream_t s) {
+  if (pages_of(p, layer) <= 0) return hipSuccess;
+  const pkv_pool_desc& d = p->desc;
+  const WindowList L = window_list(p, window);
+  const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
+  float* wdk = p->d_dk + window * p->layer_elems;
+  float* wdv = p->d_dv + window * p->layer_elems;
+  if (p->accumulate) {
+    hipLaunchKernelGGL(window_grad_zero_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count,
+                       page_elems, wdk, wdv);
+    return hipGetLastError();
+  }
+  KernelTimer t(KT_FETCH, s);
+  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
+                     page_elems, false, p->kv_bytes, nullptr, nullptr, nullptr, nullptr,
+                     d.host_grad_dtype == PKV_BF16 ? 1 : 2, (const char*)p->m_dk[layer],
+                     (const char*)p->m_dv[layer], wdk, wdv, p->d_moved);
   return hipGetLastError();
 }
 
 hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipStream_t s) {
   const pkv_pool_desc& d = p->desc;
-  const int64_t n_pages = (p->length[layer] + d.page_size - 1) / d.page_size;
-  if (n_pages <= 0) return hipSuccess;
-  const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
-  const uint8_t* need = p->d_need + (int64_t)window * d.n_kv_heads * d.max_logical_pages;
-  const int32_t* table = p->d_table + (int64_t)layer * d.n_kv_heads * d.max_logical_pages;
+  const WindowList L = window_list(p, window);
+  // the page-heads the window's last prefetch listed; their gradients go to
+  // the tier itself, or to the window's staging (same indexing) for host adds
+  void* dst_dk = p->accumulate ? p->m_stage_dk[window] : p->m_dk[layer];
+  void* dst_dv = p->accumulate ? p->m_stage_dv[window] : p->m_dv[layer];
   KernelTimer t(KT_WRITEBACK, s);
-  hipLaunchKernelGGL(writeback_kernel, dim3(kCopyBlocks), dim3(256), 0, s,
-                     need, table, d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)n_pages,
-                     page_elems, d.host_grad_dtype == PKV_BF16, p->m_dk[layer], p->m_dv[layer],
+  hipLaunchKernelGGL(writeback_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
+                     (int64_t)d.page_size * d.head_dim, d.host_grad_dtype == PKV_BF16,
+                     (char*)dst_dk, (char*)dst_dv,
                      (const float*)(p->d_dk + window * p->layer_elems),
                      (const float*)(p->d_dv + window * p->layer_elems), p->d_moved + 1);
   return hipGetLastError();

@@ -121,11 +121,16 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   }
   if (d.host_tier && d.host_grad_dtype != PKV_F32 && d.host_grad_dtype != PKV_BF16)
     return fail(PKV_EINVAL, "pkv_pool_create: host_grad_dtype must be PKV_F32 or PKV_BF16");
+  if (d.host_grad_accumulate != 0 && d.host_grad_accumulate != 1)
+    return fail(PKV_EINVAL, "pkv_pool_create: host_grad_accumulate must be 0 or 1");
+  if (d.host_grad_accumulate && !d.host_tier)
+    return fail(PKV_EINVAL, "pkv_pool_create: host_grad_accumulate needs host_tier");
 
   pkv_pool* p = new (std::nothrow) pkv_pool();
   if (!p) return fail(PKV_ENOMEM, "pkv_pool_create: out of host memory");
   p->desc = d;
   p->kv_bytes = d.kv_dtype == PKV_BF16 ? 2 : 4;
+  p->accumulate = d.host_grad_accumulate != 0;
   p->layer_elems = (int64_t)d.n_kv_heads * d.n_slots * d.page_size * d.head_dim;
   p->length.assign(d.n_layers, 0);
   p->h_table.resize((size_t)d.n_layers * d.n_kv_heads * d.max_logical_pages);

@@ -7,8 +7,11 @@
 // pinned host memory and the GPU on separate streams, the next layer being
 // fetched while the current one computes).
 #include <hip/hip_runtime.h>
+#include <sched.h>
 
+#include <cstdlib>
 #include <cstring>
+#include <exception>
 
 #include "pkv_pool.h"
 
@@ -46,6 +49,20 @@ pkv_status host_alloc(pkv_pool* p, void** hptr, void** dptr, int64_t bytes) {
 
 int grad_host_bytes(const pkv_pool* p) { return p->desc.host_grad_dtype == PKV_BF16 ? 2 : 4; }
 
+// Threads that add staged gradient contributions into the host tier: the
+// environment variable PKV_HOST_ADD_THREADS, else min(16, CPUs this process
+// may run on).
+int host_add_threads() {
+  if (const char* s = std::getenv("PKV_HOST_ADD_THREADS")) {
+    const int n = std::atoi(s);
+    return n < 1 ? 1 : (n > 64 ? 64 : n);
+  }
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  const int cpus = sched_getaffinity(0, sizeof set, &set) == 0 ? CPU_COUNT(&set) : 8;
+  return cpus < 1 ? 1 : (cpus > 16 ? 16 : cpus);
+}
+
 }  // namespace
 
 pkv_status pool_allocate(pkv_pool* p) {
@@ -56,9 +73,11 @@ pkv_status pool_allocate(pkv_pool* p) {
   const int64_t grb = p->layer_elems * 4 * copies;
   const int64_t repb = (int64_t)d.n_layers * d.n_kv_heads * d.n_slots * d.head_dim * 4;
   const int64_t tabb = (int64_t)d.n_layers * d.n_kv_heads * d.max_logical_pages * 4;
-  const int64_t needb = d.host_tier ? (int64_t)pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
+  // page maps and lists: two buffers per window
+  const int64_t needb = d.host_tier ? (int64_t)2 * pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
+  const int64_t itemb = 8 * needb + 4 * 2 * pkv_pool::kWindow;
   if (d.host_tier && d.device_budget_bytes > 0 &&
-      2 * kvb + 2 * grb + repb + tabb + needb + 16 > d.device_budget_bytes)
+      2 * kvb + 2 * grb + repb + tabb + needb + itemb + 16 > d.device_budget_bytes)
     return pool_fail(PKV_ENOMEM, "host-tier window does not fit device_budget_bytes");
   if ((st = dev_alloc(p, &p->d_k, kvb, "device allocation of the K pool failed")) != PKV_OK) return st;
   if ((st = dev_alloc(p, &p->d_v, kvb, "device allocation of the V pool failed")) != PKV_OK) return st;
@@ -75,14 +94,22 @@ pkv_status pool_allocate(pkv_pool* p) {
     return pool_hip_fail(e, "hipEventCreate");
   if (d.host_tier) {
     if ((st = dev_alloc(p, (void**)&p->d_need, needb, "device allocation of the window map failed")) != PKV_OK) return st;
+    if ((st = dev_alloc(p, (void**)&p->d_items, 8 * needb, "device allocation of the window list failed")) != PKV_OK) return st;
+    if ((st = dev_alloc(p, (void**)&p->d_count, 4 * 2 * pkv_pool::kWindow, "device allocation of the window list failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_moved, 16, "device allocation of the copy counters failed")) != PKV_OK) return st;
     for (int w = 0; w < pkv_pool::kWindow; ++w) {
       if ((e = hipEventCreateWithFlags(&p->ev_compute[w], hipEventDisableTiming)) != hipSuccess)
         return pool_hip_fail(e, "hipEventCreate");
       if ((e = hipEventCreateWithFlags(&p->ev_ready[w], hipEventDisableTiming)) != hipSuccess)
         return pool_hip_fail(e, "hipEventCreate");
-      if ((e = hipEventCreateWithFlags(&p->ev_wb[w], hipEventDisableTiming)) != hipSuccess)
+      // the host adds' coordinator waits on this one: let it sleep, not spin
+      const unsigned wb_flags =
+          hipEventDisableTiming | (p->accumulate ? hipEventBlockingSync : 0u);
+      if ((e = hipEventCreateWithFlags(&p->ev_wb[w], wb_flags)) != hipSuccess)
         return pool_hip_fail(e, "hipEventCreate");
+      for (int b = 0; b < 2; ++b)
+        if ((e = hipEventCreateWithFlags(&p->ev_list[w][b], hipEventDisableTiming)) != hipSuccess)
+          return pool_hip_fail(e, "hipEventCreate");
     }
     const int64_t hkv = p->layer_elems * p->kv_bytes;
     const int64_t hgr = p->layer_elems * grad_host_bytes(p);
@@ -107,6 +134,26 @@ pkv_status pool_allocate(pkv_pool* p) {
           (e = launch_fill_zero(p->m_dv[l], hgr, nullptr)) != hipSuccess)
         return pool_hip_fail(e, "host tier zero fill");
     }
+    if (p->accumulate) {
+      const int64_t need_w = (int64_t)d.n_kv_heads * d.max_logical_pages;
+      for (int w = 0; w < pkv_pool::kWindow; ++w) {
+        if ((st = host_alloc(p, &p->h_stage_dk[w], &p->m_stage_dk[w], hgr)) != PKV_OK) return st;
+        if ((st = host_alloc(p, &p->h_stage_dv[w], &p->m_stage_dv[w], hgr)) != PKV_OK) return st;
+        if ((e = hipHostMalloc((void**)&p->h_stage_need[w], (size_t)need_w, hipHostMallocDefault)) !=
+            hipSuccess) {
+          p->h_stage_need[w] = nullptr;
+          (void)hipGetLastError();
+          return pool_fail(PKV_ENOMEM, "pinned host allocation of the staging page map failed");
+        }
+        p->host_bytes += need_w;
+      }
+      try {
+        p->adder = new HostAdder(host_add_threads());
+      } catch (const std::exception&) {
+        p->adder = nullptr;
+        return pool_fail(PKV_ENOMEM, "could not start the host gradient add threads");
+      }
+    }
   }
   e = hipDeviceSynchronize();
   if (e != hipSuccess) return pool_hip_fail(e, "hipDeviceSynchronize (pool init)");
@@ -117,8 +164,13 @@ pkv_status pool_release(pkv_pool* p) {
   pkv_status st = PKV_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) st = pool_hip_fail(e, "hipDeviceSynchronize (pool destroy)");
+  delete p->adder;  // finishes the pending host adds
+  p->adder = nullptr;
+  for (int w = 0; w < pkv_pool::kWindow; ++w)
+    for (void* x : {p->h_stage_dk[w], p->h_stage_dv[w], (void*)p->h_stage_need[w]})
+      if (x) (void)hipHostFree(x);
   void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_delta,
-                 p->d_select, p->d_need, p->d_moved};
+                 p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved};
   for (void* x : dev)
     if (x) (void)hipFree(x);
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
@@ -131,6 +183,8 @@ pkv_status pool_release(pkv_pool* p) {
     if (p->ev_compute[w]) (void)hipEventDestroy(p->ev_compute[w]);
     if (p->ev_ready[w]) (void)hipEventDestroy(p->ev_ready[w]);
     if (p->ev_wb[w]) (void)hipEventDestroy(p->ev_wb[w]);
+    for (int b = 0; b < 2; ++b)
+      if (p->ev_list[w][b]) (void)hipEventDestroy(p->ev_list[w][b]);
   }
   return st;
 }
@@ -170,6 +224,8 @@ pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s) {
       return pool_hip_fail(e, "pkv_grad_zero");
     return PKV_OK;
   }
+  pkv_status st = pool_host_adds_wait(p);
+  if (st != PKV_OK) return st;
   const int64_t hgr = p->layer_elems * grad_host_bytes(p);
   if ((e = launch_fill_zero(p->m_dk[layer], hgr, s)) != hipSuccess ||
       (e = launch_fill_zero(p->m_dv[layer], hgr, s)) != hipSuccess)
@@ -193,6 +249,8 @@ pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s)
     e = launch_export(layer_view(p, layer), g, what, p->kv_bytes, n_tok, dst, s);
   } else {
     if ((e = hipDeviceSynchronize()) != hipSuccess) return pool_hip_fail(e, "pkv_read_pages: sync");
+    const pkv_status st = pool_host_adds_wait(p);
+    if (st != PKV_OK) return st;
     if ((what == PKV_DK || what == PKV_DV) && p->desc.host_grad_dtype == PKV_BF16)
       e = launch_host_export(p, layer, what, n_tok, dst, s);
     else
@@ -228,25 +286,40 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   const int w = p->window_of(layer);
   const pkv_pool_desc& d = p->desc;
   hipError_t e;
+  // K/V of the window are free once the attention calls on its last layer ran
   if (p->compute_recorded[w]) {
     if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
       return pool_hip_fail(e, "hipStreamWaitEvent (window reuse)");
   }
-  if (p->wb_recorded[w]) {
-    if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
-      return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
+  // build the other list buffer, once the writeback that last read it ran
+  const int b = p->list_gen[w] ^ 1;
+  if (p->list_recorded[w][b]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_list[w][b], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (window list)");
   }
-  uint8_t* need = p->d_need + (int64_t)w * d.n_kv_heads * d.max_logical_pages;
+  p->list_gen[w] = b;
+  const int64_t nw = need_words(p);
+  uint8_t* need = p->d_need + (int64_t)(w * 2 + b) * nw;
   // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every appended key)
   const int64_t n_avail = n_keys > 0 && n_keys < p->length[layer] ? n_keys : p->length[layer];
   const int64_t n_pages = (n_avail + d.page_size - 1) / d.page_size;
-  if ((e = launch_need_clear(need, (int64_t)d.n_kv_heads * d.max_logical_pages, cs)) != hipSuccess ||
-      (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess)
+  if ((e = launch_need_clear(need, nw, cs)) != hipSuccess ||
+      (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess ||
+      (e = launch_window_list(p, layer, w, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");
   p->window_layer[w] = layer;
   p->window_grads[w] = with_grads;
-  if ((e = launch_fetch_pages(p, layer, w, with_grads, cs)) != hipSuccess)
+  if ((e = launch_fetch_kv(p, layer, w, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
+  if (with_grads) {
+    // the window's gradients are free once its last writeback read them
+    if (p->wb_recorded[w]) {
+      if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
+        return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
+    }
+    if ((e = launch_fetch_grads(p, layer, w, cs)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_prefetch_pages: gradient fetch");
+  }
   if ((e = hipEventRecord(p->ev_ready[w], cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (window ready)");
   p->ready_recorded[w] = true;
@@ -265,11 +338,50 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
     if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
       return pool_hip_fail(e, "hipStreamWaitEvent (writeback)");
   }
+  // the prefetch filled the window on its own stream
+  if (p->ready_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_ready[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (writeback after prefetch)");
+  }
+  if (p->accumulate) {
+    // the staging of window w is free once the adds of its last writeback ran
+    if ((e = p->adder->wait(p->stage_ticket[w])) != hipSuccess)
+      return pool_hip_fail(e, "host gradient adds: hipEventSynchronize");
+  }
   if ((e = launch_writeback_pages(p, layer, w, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_writeback_grads: launch");
+  const pkv_pool_desc& d = p->desc;
+  const int64_t need_w = need_words(p);
+  const int b = p->list_gen[w];
+  if (p->accumulate &&
+      (e = hipMemcpyAsync(p->h_stage_need[w], p->d_need + (int64_t)(w * 2 + b) * need_w,
+                          (size_t)need_w, hipMemcpyDeviceToHost, cs)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_writeback_grads: page map copy");
+  if ((e = hipEventRecord(p->ev_list[w][b], cs)) != hipSuccess)
+    return pool_hip_fail(e, "hipEventRecord (window list)");
+  p->list_recorded[w][b] = true;
   if ((e = hipEventRecord(p->ev_wb[w], cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (writeback)");
   p->wb_recorded[w] = true;
+  if (p->accumulate) {
+    AddJob job;
+    job.ready = p->ev_wb[w];
+    job.need = p->h_stage_need[w];
+    const int32_t* tab = p->h_table.data() + (int64_t)layer * need_w;
+    job.table.assign(tab, tab + need_w);
+    job.hkv = d.n_kv_heads;
+    job.max_logical = d.max_logical_pages;
+    job.n_pages = (int)((p->length[layer] + d.page_size - 1) / d.page_size);
+    job.slots = d.n_slots;
+    job.page_elems = (int64_t)d.page_size * d.head_dim;
+    job.bf16 = d.host_grad_dtype == PKV_BF16;
+    job.src_dk = p->h_stage_dk[w];
+    job.src_dv = p->h_stage_dv[w];
+    job.dst_dk = p->h_dk[layer];
+    job.dst_dv = p->h_dv[layer];
+    p->stage_ticket[w] = p->adder->submit(job);
+    p->window_grads[w] = false;  // a second writeback would add the same contributions again
+  }
   if (done && (e = hipEventRecord(done, cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (writeback done)");
   return PKV_OK;
@@ -279,11 +391,20 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
 
 namespace pkv {
 
+pkv_status pool_host_adds_wait(pkv_pool* p) {
+  if (!p->adder) return PKV_OK;
+  const hipError_t e = p->adder->drain();
+  if (e != hipSuccess) return pool_hip_fail(e, "host gradient adds: hipEventSynchronize");
+  return PKV_OK;
+}
+
 pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written) {
   unsigned long long h[2] = {0, 0};
   if (p->d_moved) {
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return pool_hip_fail(e, "pkv_offload_bytes: sync");
+    const pkv_status st = pool_host_adds_wait(p);
+    if (st != PKV_OK) return st;
     e = hipMemcpy(h, p->d_moved, sizeof h, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return pool_hip_fail(e, "pkv_offload_bytes: copy");
   }

@@ -7,6 +7,7 @@
 
 #include <vector>
 
+#include "host_add.h"
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -48,8 +49,31 @@ struct pkv_pool {
   bool wb_recorded[kWindow] = {false, false};
   bool compute_recorded[kWindow] = {false, false};
   bool ready_recorded[kWindow] = {false, false};
-  uint8_t* d_need = nullptr;      // [kWindow][Hkv][max_logical] pages held by the window
+  // Page map and list of each window, double-buffered: a prefetch builds
+  // buffer list_gen[w] ^ 1 while the window's last writeback may still read
+  // buffer list_gen[w]; ev_list[w][b] is recorded after the writeback that
+  // read buffer b.
+  uint8_t* d_need = nullptr;      // [kWindow][2][Hkv][max_logical] page-heads held by the window
+  int64_t* d_items = nullptr;     // [kWindow][2][Hkv * max_logical] their element offsets, listed
+  int* d_count = nullptr;         // [kWindow][2] list lengths
+  int list_gen[kWindow] = {0, 0};
+  hipEvent_t ev_list[kWindow][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+  bool list_recorded[kWindow][2] = {{false, false}, {false, false}};
   unsigned long long* d_moved = nullptr;  // [0] bytes fetched, [1] bytes written back
+
+  // host_grad_accumulate: window gradients start at zero on every prefetch;
+  // a writeback stages the visit's contributions (host gradient dtype,
+  // indexed like the tier) and the window's page map in pinned memory, and
+  // `adder` adds them into the layer's host gradients.  stage_ticket[w] is
+  // the add job that still reads window w's staging.
+  bool accumulate = false;
+  void* h_stage_dk[kWindow] = {nullptr, nullptr};
+  void* h_stage_dv[kWindow] = {nullptr, nullptr};
+  void* m_stage_dk[kWindow] = {nullptr, nullptr};   // device-visible aliases
+  void* m_stage_dv[kWindow] = {nullptr, nullptr};
+  uint8_t* h_stage_need[kWindow] = {nullptr, nullptr};
+  int64_t stage_ticket[kWindow] = {0, 0};
+  pkv::HostAdder* adder = nullptr;
 
   int window_of(int layer) const { return layer % kWindow; }
 };
@@ -79,9 +103,12 @@ pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written);
 hipError_t launch_need_clear(uint8_t* need, int64_t n, hipStream_t s);
 hipError_t launch_need_mark(uint8_t* need, const pkv_sel* sel, int hkv, int max_logical,
                             int64_t n_pages_all, hipStream_t s);
-hipError_t launch_fetch_pages(const pkv_pool* p, int layer, int window, bool with_grads,
-                              hipStream_t s);
+int64_t need_words(const pkv_pool* p);  // Hkv * max_logical
+hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStream_t s);
+hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s);
+hipError_t launch_fetch_grads(const pkv_pool* p, int layer, int window, hipStream_t s);
 hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipStream_t s);
+pkv_status pool_host_adds_wait(pkv_pool* p);
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,
                               hipStream_t s);
 

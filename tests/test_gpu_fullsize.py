@@ -153,14 +153,16 @@ def test_qwen_256k_topk_full():
     _check(cfg, got, heads=(0, 15), key_tail=32, sel_chunks=picked)
 
 
-def test_qwen_1m_offload_last_chunk():
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_qwen_1m_offload_last_chunk(accumulate):
     """The 1M-token top-K workload with every pool in the host tier (2 of its
     28 layers: the per-layer path is the same for every layer, and the box
     pins at most 64 GiB per process): the backward sweep of the last chunk
     through OffloadSweep (select one layer ahead, prefetch on a side stream,
     gradient writeback), checked per layer against the oracle on the
     selection of the chunk, sampled rows (O, LSE, dQ) and the last keys'
-    dK/dV in full, which only the last chunk's rows reach."""
+    dK/dV in full, which only the last chunk's rows reach.  accumulate=1: the
+    gradient contributions are added into the host tier by host threads."""
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -171,7 +173,8 @@ def test_qwen_1m_offload_last_chunk():
     ws = [GpuWorkload(cfg, layer=l) for l in range(L)]
     pool = pkv.pkv_pool_create(L, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16,
                                host_tier=1, host_grad_dtype=pkv.PKV_BF16,
-                               device_budget_bytes=cfg.hbm_cap_bytes)
+                               device_budget_bytes=cfg.hbm_cap_bytes,
+                               host_grad_accumulate=accumulate)
     for l in range(L):
         tab = ws[l].table()
         for g in range(cfg.hkv):
@@ -238,6 +241,7 @@ def test_qwen_1m_offload_last_chunk():
         worst[f"dv_tail{l}"] = rel_err(dv.cpu().numpy()[s0:], rdv)
         del k, v
     pool.close()
-    print(cfg.name, {k_: f"{v_:.2e}" for k_, v_ in worst.items()}, flush=True)
+    print(cfg.name, f"host adds {accumulate}", {k_: f"{v_:.2e}" for k_, v_ in worst.items()},
+          flush=True)
     for name, e in worst.items():
         assert e <= 1e-2, f"{name}: {e:.3e}"
