@@ -450,13 +450,19 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
         torch.cuda.synchronize()
         windows = []  # (first chunk id of the window, chunks done, bytes fetched, written) so far
         t0 = time.perf_counter()
-        for n_done, c in enumerate(chunk_ids):
+        def bufs_for(c):
             n = cfg.chunk_range(c)[1]
             if n not in bufsets:
                 bufsets[n] = {l: ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page,
                                               torch.bfloat16, sp) for l in range(2)}
-            bufs = {l: bufsets[n][l % 2] for l in range(L)}
-            sweep.chunk(c, inputs, bufs)
+            return {l: bufsets[n][l % 2] for l in range(L)}
+
+        for n_done, c in enumerate(chunk_ids):
+            # the next chunk's top layer is selected and prefetched during this
+            # chunk's layer 0
+            nxt = chunk_ids[n_done + 1] if n_done + 1 < len(chunk_ids) else None
+            sweep.chunk(c, inputs, bufs_for(c),
+                        next_chunk=(nxt, bufs_for(nxt)) if nxt is not None else None)
             if n_done % 8 == 7:
                 torch.cuda.synchronize()
                 fb, wb = pkv.pkv_offload_bytes(pool)

@@ -109,27 +109,42 @@ class OffloadSweep:
         else:
             pkv_prefetch_pages(self.pool, layer, sel, with_grads=True, copy_stream=self.copy)
 
-    def chunk(self, c: int, inputs, bufs, outputs=None):
-        """Backward-sweep step of chunk c over every layer.  bufs[layer]:
-        ChunkBuffers sized for this chunk (two alternating sets suffice).
-        outputs(layer, c, buf) is called after the layer's backward is
-        enqueued (on the compute stream) to collect results."""
-        from . import pkv_writeback_grads
-        L = self.L
-        ins = {L - 1: inputs(L - 1, c)}
-        sel = self._select(L - 1, ins[L - 1], bufs[L - 1])
+    def _select_and_prefetch(self, layer: int, ch: dict, buf):
+        sel = self._select(layer, ch, buf)
         ev = torch.cuda.Event()
         ev.record(self.compute)
         self.copy.wait_event(ev)
-        self._prefetch(L - 1, ins[L - 1], sel)
+        self._prefetch(layer, ch, sel)
+
+    def chunk(self, c: int, inputs, bufs, outputs=None, next_chunk=None):
+        """Backward-sweep step of chunk c over every layer.  bufs[layer]:
+        ChunkBuffers sized for this chunk (two alternating sets suffice).
+        outputs(layer, c, buf) is called after the layer's backward is
+        enqueued (on the compute stream) to collect results.
+
+        next_chunk = (c_next, bufs_next): the chunk the caller runs next and
+        its buffers.  While layer 0 of chunk c computes, the top layer of
+        c_next is selected and prefetched, so that the next call does not
+        start with a fetch that nothing overlaps (only when the two layers
+        use different windows, i.e. an even number of layers)."""
+        from . import pkv_writeback_grads
+        L = self.L
+        ahead = getattr(self, "_ahead", None)
+        self._ahead = None
+        if ahead is not None and ahead[0] == c:
+            ins = {L - 1: ahead[1]}
+        else:
+            ins = {L - 1: inputs(L - 1, c)}
+            self._select_and_prefetch(L - 1, ins[L - 1], bufs[L - 1])
         for layer in range(L - 1, -1, -1):
             if layer - 1 >= 0:
                 ins[layer - 1] = inputs(layer - 1, c)
-                nsel = self._select(layer - 1, ins[layer - 1], bufs[layer - 1])
-                ev = torch.cuda.Event()
-                ev.record(self.compute)
-                self.copy.wait_event(ev)
-                self._prefetch(layer - 1, ins[layer - 1], nsel)
+                self._select_and_prefetch(layer - 1, ins[layer - 1], bufs[layer - 1])
+            elif next_chunk is not None and L % 2 == 0:
+                c_next, bufs_next = next_chunk
+                ch_next = inputs(L - 1, c_next)
+                self._select_and_prefetch(L - 1, ch_next, bufs_next[L - 1])
+                self._ahead = (c_next, ch_next)
             ch, b = ins.pop(layer), bufs[layer]
             pkv_attn_fwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, b.lse, self.scale,
                          sel=b.sel, stream=self.compute)

@@ -286,7 +286,7 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   if (n_q == 0) return PKV_OK;
   if (!q || !o || !lse) return fail(PKV_EINVAL, "pkv_attn_fwd: null q/o/lse");
   if ((st = check_sel(pool, sel, n_q, "pkv_attn_fwd")) != PKV_OK) return st;
-  if ((st = pool_before_compute(pool, layer, stream)) != PKV_OK) return st;
+  if ((st = pool_before_compute(pool, layer, stream, false)) != PKV_OK) return st;
   AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
   c.q = q;
   c.o_out = o;
@@ -314,7 +314,7 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   if (plan) pl = dkdv_plan_layout(geom(pool), n_q_heads, q_pos0, (int)n_q, sel->stride);
   if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes, dl_bytes + pl.bytes)) != PKV_OK)
     return st;
-  if ((st = pool_before_compute(pool, layer, stream)) != PKV_OK) return st;
+  if ((st = pool_before_compute(pool, layer, stream, true)) != PKV_OK) return st;
   AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
   c.q = q;
   c.o = o;

@@ -260,7 +260,20 @@ pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s)
   return PKV_OK;
 }
 
-pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s) {
+// Zero the window's listed gradient pages on stream s if the visit still
+// needs it (host accumulation), after the window's previous writeback.
+static pkv_status zero_window_grads(pkv_pool* p, int layer, int w, hipStream_t s) {
+  if (!p->zero_pending[w]) return PKV_OK;
+  hipError_t e;
+  if (p->wb_recorded[w] && (e = hipStreamWaitEvent(s, p->ev_wb[w], 0)) != hipSuccess)
+    return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
+  if ((e = launch_fetch_grads(p, layer, w, s)) != hipSuccess)
+    return pool_hip_fail(e, "window gradient zero");
+  p->zero_pending[w] = false;
+  return PKV_OK;
+}
+
+pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s, bool grads) {
   if (!p->desc.host_tier) return PKV_OK;
   const int w = p->window_of(layer);
   if (p->window_layer[w] != layer)
@@ -269,7 +282,7 @@ pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s) {
     hipError_t e = hipStreamWaitEvent(s, p->ev_ready[w], 0);
     if (e != hipSuccess) return pool_hip_fail(e, "hipStreamWaitEvent (window ready)");
   }
-  return PKV_OK;
+  return grads ? zero_window_grads(p, layer, w, s) : PKV_OK;
 }
 
 pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s) {
@@ -311,7 +324,8 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   p->window_grads[w] = with_grads;
   if ((e = launch_fetch_kv(p, layer, w, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
-  if (with_grads) {
+  p->zero_pending[w] = with_grads && p->accumulate;
+  if (with_grads && !p->accumulate) {
     // the window's gradients are free once its last writeback read them
     if (p->wb_recorded[w]) {
       if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
@@ -344,6 +358,9 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
       return pool_hip_fail(e, "hipStreamWaitEvent (writeback after prefetch)");
   }
   if (p->accumulate) {
+    // no attention backward since the prefetch: the contributions are zeros
+    const pkv_status st = zero_window_grads(p, layer, w, cs);
+    if (st != PKV_OK) return st;
     // the staging of window w is free once the adds of its last writeback ran
     if ((e = p->adder->wait(p->stage_ticket[w])) != hipSuccess)
       return pool_hip_fail(e, "host gradient adds: hipEventSynchronize");

@@ -73,6 +73,10 @@ struct pkv_pool {
   void* m_stage_dv[kWindow] = {nullptr, nullptr};
   uint8_t* h_stage_need[kWindow] = {nullptr, nullptr};
   int64_t stage_ticket[kWindow] = {0, 0};
+  // the window's gradient pages still have to be zeroed: done on the stream
+  // of the first attention backward (or writeback) of the visit, so that the
+  // prefetch stream never waits for the window's previous writeback
+  bool zero_pending[kWindow] = {false, false};
   pkv::HostAdder* adder = nullptr;
 
   int window_of(int layer) const { return layer % kWindow; }
@@ -92,7 +96,7 @@ pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, cons
                        const void* v, hipStream_t s);
 pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s);
-pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s);
+pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s, bool grads);
 pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_keys, bool with_grads,
                          hipStream_t copy_stream, hipEvent_t ready);

@@ -29,7 +29,7 @@ CFG = mini_config("qwen_1m_offload", n_ctx=4096, chunk=1024, n_layers=3, top_k=6
                   slots=32)
 
 
-def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0):
+def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0, lookahead=False):
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -64,10 +64,17 @@ def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0):
         got[(l, c)] = dict(O=b.o.float().cpu(), lse=b.lse.cpu(), dq=b.dq.cpu(),
                            sel=(b.sel[0].cpu(), b.sel[1].cpu()) if sparse else None)
 
-    for c in reversed(range(cfg.n_chunks)):
-        bufs = {l: ChunkBuffers(chunks[(l, c)].n_q, cfg.hq, cfg.hkv, cfg.d, cfg.page,
+    def bufs_for(c):
+        return {l: ChunkBuffers(chunks[(l, c)].n_q, cfg.hq, cfg.hkv, cfg.d, cfg.page,
                                 torch.bfloat16, sp) for l in range(L)}
-        sweep.chunk(c, inputs, bufs, outputs)
+
+    order = list(reversed(range(cfg.n_chunks)))
+    nxt = bufs_for(order[0])
+    for i, c in enumerate(order):
+        bufs, nxt = nxt, (bufs_for(order[i + 1]) if i + 1 < len(order) else None)
+        # lookahead: the next chunk's top layer is prefetched during layer 0
+        ahead = (order[i + 1], nxt) if lookahead and nxt is not None else None
+        sweep.chunk(c, inputs, bufs, outputs, next_chunk=ahead)
     torch.cuda.synchronize()
     grads = {}
     for l in range(L):
@@ -198,10 +205,13 @@ def test_attention_before_prefetch_is_an_error():
 def test_host_accumulated_grads_match_oracle(sparse):
     """host_grad_accumulate: same O, LSE, dQ and selections as the all-HBM
     sweep; dK/dV within the bf16 bound of the oracle (contribution and sum
-    are each rounded to bf16 per visit); no gradient bytes fetched."""
+    are each rounded to bf16 per visit); no gradient bytes fetched.  Both
+    offloaded sweeps prefetch the next chunk's top layer during layer 0."""
     cfg = CFG.replace(n_layers=2)
-    off, goff, _, (_, host_a, (fetched_a, written_a)) = _sweep(cfg, True, sparse=sparse, accumulate=1)
-    _, gfetch, _, (_, host_f, (fetched_f, written_f)) = _sweep(cfg, True, sparse=sparse)
+    off, goff, _, (_, host_a, (fetched_a, written_a)) = _sweep(cfg, True, sparse=sparse, accumulate=1,
+                                                               lookahead=True)
+    _, gfetch, _, (_, host_f, (fetched_f, written_f)) = _sweep(cfg, True, sparse=sparse,
+                                                               lookahead=True)
     res, _, _, _ = _sweep(cfg, False, sparse=sparse)
     for key in res:
         for name in ("O", "lse", "dq"):
