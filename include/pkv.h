@@ -243,11 +243,15 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
  * every appended page) from pinned host memory into the HBM window, on
  * copy_stream, without a host synchronisation (de 2.C: prefetch of the next
  * layer while the current one computes).  with_grads != 0 also brings the
- * pages' dK/dV (host gradient dtype -> fp32).  The window slot the layer
- * lands in is not overwritten before earlier attention calls that read it
- * have finished (the library orders this with events).  `ready`, if not
- * NULL, is recorded on copy_stream when the copies are done; attention calls
- * on this layer wait for it on their own stream automatically. */
+ * pages' dK/dV (host gradient dtype -> fp32); with host_grad_accumulate it
+ * instead zeroes them in the window, on the stream of the layer's first
+ * attention backward (or writeback) after the prefetch.  The window slot
+ * the layer lands in is not overwritten before earlier attention calls that
+ * read it have finished, nor its gradients before the window's previous
+ * pkv_writeback_grads has read them (the library orders this with events;
+ * that writeback must have been called before this prefetch).  `ready`, if
+ * not NULL, is recorded on copy_stream when the copies are done; attention
+ * calls on this layer wait for it on their own stream automatically. */
 pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
                               int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready);
 

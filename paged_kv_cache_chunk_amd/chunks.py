@@ -71,8 +71,9 @@ class OffloadSweep:
     pages (and their gradients) are prefetched on the copy stream while the
     current layer's forward + backward run, and each layer's gradient pages
     are written back on a third stream after its backward.  Only events
-    order the streams; the host never waits on the device inside the
-    sweep.
+    order the streams; the host never waits on the device inside the sweep,
+    except that with host_grad_accumulate a writeback first waits until the
+    host adds of its window's previous writeback have freed the staging.
 
     inputs(layer, chunk) -> dict(q_pos0, q, do) of device tensors.
     """
