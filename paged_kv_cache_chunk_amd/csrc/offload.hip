@@ -295,17 +295,21 @@ hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s) {
+hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s,
+                           bool with_grads) {
   if (pages_of(p, layer) <= 0) return hipSuccess;
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
+  const int grad_mode = with_grads ? (d.host_grad_dtype == PKV_BF16 ? 1 : 2) : 0;
   KernelTimer t(KT_FETCH, s);
   hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
                      (int64_t)d.page_size * d.head_dim, true, p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
                      (char*)p->d_k + window * p->layer_elems * p->kv_bytes,
-                     (char*)p->d_v + window * p->layer_elems * p->kv_bytes, 0, nullptr, nullptr,
-                     nullptr, nullptr, p->d_moved);
+                     (char*)p->d_v + window * p->layer_elems * p->kv_bytes, grad_mode,
+                     (const char*)p->m_dk[layer], (const char*)p->m_dv[layer],
+                     p->d_dk + window * p->layer_elems, p->d_dv + window * p->layer_elems,
+                     p->d_moved);
   return hipGetLastError();
 }
 

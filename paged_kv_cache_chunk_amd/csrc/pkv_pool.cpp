@@ -322,18 +322,19 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");
   p->window_layer[w] = layer;
   p->window_grads[w] = with_grads;
-  if ((e = launch_fetch_kv(p, layer, w, cs)) != hipSuccess)
+  // Gradients fetched into HBM (no host accumulation): one launch for K/V and
+  // gradients after the window's last writeback has read its gradients.
+  // Fetching K/V before that wait and the gradients after it ran the K/V
+  // reads beside the writeback's host writes and made the 1M-token top-K
+  // sweep slower.
+  const bool grads_now = with_grads && !p->accumulate;
+  if (grads_now && p->wb_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
+  }
+  if ((e = launch_fetch_kv(p, layer, w, cs, grads_now)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
   p->zero_pending[w] = with_grads && p->accumulate;
-  if (with_grads && !p->accumulate) {
-    // the window's gradients are free once its last writeback read them
-    if (p->wb_recorded[w]) {
-      if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
-        return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
-    }
-    if ((e = launch_fetch_grads(p, layer, w, cs)) != hipSuccess)
-      return pool_hip_fail(e, "pkv_prefetch_pages: gradient fetch");
-  }
   if ((e = hipEventRecord(p->ev_ready[w], cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (window ready)");
   p->ready_recorded[w] = true;
