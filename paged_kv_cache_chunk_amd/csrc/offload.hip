@@ -295,8 +295,8 @@ hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s,
-                           bool with_grads) {
+hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
+                        bool with_grads) {
   if (pages_of(p, layer) <= 0) return hipSuccess;
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
@@ -313,23 +313,13 @@ hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_fetch_grads(const pkv_pool* p, int layer, int window, hipStream_t s) {
+hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hipStream_t s) {
   if (pages_of(p, layer) <= 0) return hipSuccess;
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
-  const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
-  float* wdk = p->d_dk + window * p->layer_elems;
-  float* wdv = p->d_dv + window * p->layer_elems;
-  if (p->accumulate) {
-    hipLaunchKernelGGL(window_grad_zero_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count,
-                       page_elems, wdk, wdv);
-    return hipGetLastError();
-  }
-  KernelTimer t(KT_FETCH, s);
-  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
-                     page_elems, false, p->kv_bytes, nullptr, nullptr, nullptr, nullptr,
-                     d.host_grad_dtype == PKV_BF16 ? 1 : 2, (const char*)p->m_dk[layer],
-                     (const char*)p->m_dv[layer], wdk, wdv, p->d_moved);
+  hipLaunchKernelGGL(window_grad_zero_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count,
+                     (int64_t)d.page_size * d.head_dim, p->d_dk + window * p->layer_elems,
+                     p->d_dv + window * p->layer_elems);
   return hipGetLastError();
 }
 

@@ -267,7 +267,7 @@ static pkv_status zero_window_grads(pkv_pool* p, int layer, int w, hipStream_t s
   hipError_t e;
   if (p->wb_recorded[w] && (e = hipStreamWaitEvent(s, p->ev_wb[w], 0)) != hipSuccess)
     return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
-  if ((e = launch_fetch_grads(p, layer, w, s)) != hipSuccess)
+  if ((e = launch_window_grad_zero(p, layer, w, s)) != hipSuccess)
     return pool_hip_fail(e, "window gradient zero");
   p->zero_pending[w] = false;
   return PKV_OK;
@@ -332,7 +332,7 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
     if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
       return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
   }
-  if ((e = launch_fetch_kv(p, layer, w, cs, grads_now)) != hipSuccess)
+  if ((e = launch_fetch(p, layer, w, cs, grads_now)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
   p->zero_pending[w] = with_grads && p->accumulate;
   if ((e = hipEventRecord(p->ev_ready[w], cs)) != hipSuccess)

@@ -109,9 +109,9 @@ hipError_t launch_need_mark(uint8_t* need, const pkv_sel* sel, int hkv, int max_
                             int64_t n_pages_all, hipStream_t s);
 int64_t need_words(const pkv_pool* p);  // Hkv * max_logical
 hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStream_t s);
-hipError_t launch_fetch_kv(const pkv_pool* p, int layer, int window, hipStream_t s,
-                           bool with_grads);
-hipError_t launch_fetch_grads(const pkv_pool* p, int layer, int window, hipStream_t s);
+hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
+                        bool with_grads);
+hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hipStream_t s);
 hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipStream_t s);
 pkv_status pool_host_adds_wait(pkv_pool* p);
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,
