@@ -93,7 +93,9 @@ def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0, look
 def test_offloaded_matches_resident_and_oracle():
     import paged_kv_cache_chunk_amd as pkv
     cfg = CFG
-    off, goff, chunks, (dev_b, host_b, _) = _sweep(cfg, True)
+    # three layers: the next chunk's top layer would share layer 0's window,
+    # so the sweep must fall back to prefetching it at the chunk's start
+    off, goff, chunks, (dev_b, host_b, _) = _sweep(cfg, True, lookahead=True)
     res, gres, _, (dev_r, host_r, _) = _sweep(cfg, False)
     # memory: the host tier holds every layer, HBM only the two-layer window
     assert host_b > 0 and host_r == 0
@@ -131,7 +133,7 @@ def test_offloaded_dense_matches_resident_and_oracle():
     """Dense chunks prefetch only the pages of keys up to their last query
     (pkv_prefetch_prefix) and write back the same pages' gradients."""
     cfg = CFG.replace(n_layers=2)
-    off, goff, _, _ = _sweep(cfg, True, sparse=False)
+    off, goff, _, _ = _sweep(cfg, True, sparse=False, lookahead=True)
     res, gres, _, _ = _sweep(cfg, False, sparse=False)
     for key in res:
         for name in ("O", "lse", "dq"):
