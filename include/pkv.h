@@ -89,9 +89,21 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *   n_slots      slots per layer per KV head (>= max_logical_pages).
  *   host_tier    0: all pools in HBM.  1: K, V, dK, dV of every layer live in
  *                pinned host memory (K/V in kv_dtype, gradients in
- *                host_grad_dtype) and HBM holds a window of two layers that
- *                pkv_prefetch_pages fills; representatives and page tables
- *                stay in HBM.
+ *                host_grad_dtype) and HBM holds two windows (layers of
+ *                even / odd index) that pkv_prefetch_pages fills;
+ *                representatives and page tables stay in HBM.
+ *   window_slots host-tier only (else 0): page slots per KV head in each
+ *                HBM window; 0 means max_logical_pages (a whole layer).  A
+ *                prefetch places the page-heads it brings in the first free
+ *                slots of its window, so the window bounds the pages one
+ *                visit can hold, not the context: HBM use is then
+ *                2 x Hkv x window_slots x P x d x (2 kv bytes + 8) plus the
+ *                representatives and page tables, whatever
+ *                max_logical_pages is ("Out of the Memory Barrier",
+ *                gist.science de, section 4: memory grows by ~10 MB per 10K
+ *                tokens; section 2.D: with page top-K only the selected
+ *                pages move).  A prefetch whose pages could exceed it is
+ *                rejected (PKV_ECAPACITY; see pkv_prefetch_pages).
  *   host_grad_dtype  host-tier gradient storage (PKV_F32 or PKV_BF16).
  *   host_grad_accumulate  host-tier only (else PKV_EINVAL).  0: a prefetch
  *                with grads brings the pages' accumulated dK/dV into HBM
@@ -125,6 +137,7 @@ typedef struct {
   int32_t host_tier;       /* 0 or 1 */
   int32_t host_grad_dtype; /* pkv_dtype, host-tier only */
   int32_t host_grad_accumulate; /* 0 or 1, host-tier only */
+  int32_t window_slots;    /* host-tier only: HBM slots per KV head per window */
   int64_t device_budget_bytes;
 } pkv_pool_desc;
 
@@ -251,7 +264,15 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
  * pkv_writeback_grads has read them (the library orders this with events;
  * that writeback must have been called before this prefetch).  `ready`, if
  * not NULL, is recorded on copy_stream when the copies are done; attention
- * calls on this layer wait for it on their own stream automatically. */
+ * calls on this layer wait for it on their own stream automatically.
+ * The window then covers the keys appended so far: attention calls on the
+ * layer whose queries reach past them (tokens appended after the prefetch)
+ * return PKV_ESTATE until the layer is prefetched again, and a backward
+ * after a prefetch without gradients (or after the visit's
+ * pkv_writeback_grads) returns PKV_ESTATE.  With a window smaller than a
+ * layer, the pages a selection can name per KV head, min(n_qpages x stride,
+ * pages appended), must fit window_slots, else PKV_ECAPACITY and nothing
+ * is enqueued. */
 pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
                               int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready);
 
@@ -262,7 +283,8 @@ pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
  * changes (de 2.C: prefetch of the next layer's KV; the chunk attends to
  * every earlier page plus its own, de 2.A).  pkv_writeback_grads then writes
  * back the same pages.  1 <= n_keys <= the layer's appended length, else
- * PKV_EINVAL. */
+ * PKV_EINVAL; ceil(n_keys / P) pages must fit window_slots, else
+ * PKV_ECAPACITY. */
 pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t with_grads,
                                hipStream_t copy_stream, hipEvent_t ready);
 

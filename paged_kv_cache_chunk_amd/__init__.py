@@ -45,7 +45,7 @@ class pkv_pool_desc(ctypes.Structure):
         ("max_logical_pages", ctypes.c_int32), ("n_slots", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32), ("host_tier", ctypes.c_int32),
         ("host_grad_dtype", ctypes.c_int32), ("host_grad_accumulate", ctypes.c_int32),
-        ("device_budget_bytes", ctypes.c_int64),
+        ("window_slots", ctypes.c_int32), ("device_budget_bytes", ctypes.c_int64),
     ]
 
 
@@ -165,10 +165,11 @@ class Pool:
 def pkv_pool_create(n_layers: int, n_kv_heads: int, head_dim: int, page_size: int,
                     max_logical_pages: int, n_slots: int, kv_dtype: int,
                     host_tier: int = 0, host_grad_dtype: int = PKV_BF16,
-                    device_budget_bytes: int = 0, host_grad_accumulate: int = 0) -> Pool:
+                    device_budget_bytes: int = 0, host_grad_accumulate: int = 0,
+                    window_slots: int = 0) -> Pool:
     d = pkv_pool_desc(n_layers, n_kv_heads, head_dim, page_size, max_logical_pages, n_slots,
                       kv_dtype, host_tier, host_grad_dtype, host_grad_accumulate,
-                      device_budget_bytes)
+                      window_slots, device_budget_bytes)
     h = ctypes.c_void_p()
     _check(lib().pkv_pool_create(ctypes.byref(d), ctypes.byref(h)))
     return Pool(h.value, d)

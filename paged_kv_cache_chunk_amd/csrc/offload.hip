@@ -6,8 +6,11 @@
 // nl, "Methodologie", asynchronous CPU offloading; de 2.D: page-level
 // sparsity also shrinks the offload traffic, because only the selected pages
 // move).  The union of the pages a selection names is marked in a per-window
-// byte map, which one small kernel turns into a list of page-heads; the copy
-// kernels stream over that list.  Gradients travel as the host gradient dtype and live in HBM as
+// byte map, which one small kernel turns into a list of page-heads and the
+// window's table: the window holds a fixed number of slots per KV head and
+// each visit packs its pages into the first ones, so its size bounds the
+// pages of one visit, not the context.  The copy kernels stream over the
+// list.  Gradients travel as the host gradient dtype and live in HBM as
 // fp32 while the layer computes; with host accumulation they are not
 // fetched but zeroed in the window, and the writeback sends the window's
 // contributions to a pinned staging area instead of the tier.  Two device
@@ -42,35 +45,61 @@ __global__ void need_mark_all_kernel(uint8_t* need, int max_logical, int64_t n_p
   if (j < n_pages) need[(int64_t)blockIdx.y * max_logical + j] = 1;
 }
 
-// The marked page-heads of a window as a dense list of element offsets
-// (page-major, then KV head), and its length: one workgroup, a block scan
-// over the map.  The copy kernels then stream over the list without
-// touching the map or the page table again.
+// The marked page-heads of a window as a dense list, and the window's table:
+// one workgroup, one block scan over the map per KV head.  The j-th marked
+// page of head g (in page order) takes window slot j of that head; a list
+// entry holds the page-head's index in the tier (g * n_slots + its slot in
+// the layer's table) and in the window (g * wslots + window slot), so the
+// copy kernels stream over the list without touching the map or a table
+// again.  Pages the window does not hold map to window slot 0 of their head
+// (a selection that names only listed pages never reaches them).  The host
+// checks before the launch that no head marks more than wslots pages; a
+// page past that bound would be left out, never written out of bounds.
 __global__ void __launch_bounds__(1024) need_compact_kernel(
     const uint8_t* __restrict__ need, const int32_t* __restrict__ table, int max_logical,
-    int slots, int hkv, int n_pages, int64_t page_elems, int64_t* __restrict__ items,
-    int* __restrict__ count) {
+    int n_slots, int hkv, int n_pages, int wslots, int2* __restrict__ items,
+    int* __restrict__ count, int32_t* __restrict__ wtable) {
   __shared__ int s_sum[1024];
-  const int64_t n = (int64_t)n_pages * hkv;
+  __shared__ int s_base;
   const int tid = threadIdx.x, T = blockDim.x;
-  const int64_t per = (n + T - 1) / T;
-  const int64_t lo = tid * per, hi = lo + per < n ? lo + per : n;
-  int c = 0;
-  for (int64_t i = lo; i < hi; ++i) c += need[(i % hkv) * max_logical + i / hkv] != 0;
-  s_sum[tid] = c;
+  const int per = (n_pages + T - 1) / T;
+  const int lo = tid * per < n_pages ? tid * per : n_pages;
+  const int hi = lo + per < n_pages ? lo + per : n_pages;
+  if (tid == 0) s_base = 0;
+  for (int g = 0; g < hkv; ++g) {
+    const uint8_t* ng = need + (int64_t)g * max_logical;
+    int c = 0;
+    for (int j = lo; j < hi; ++j) c += ng[j] != 0;
+    __syncthreads();  // s_base of the previous head is in place
+    const int base = s_base;
+    s_sum[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < T; off <<= 1) {
+      const int add = tid >= off ? s_sum[tid - off] : 0;
+      __syncthreads();
+      s_sum[tid] += add;
+      __syncthreads();
+    }
+    int pos = s_sum[tid] - c;
+    int32_t* wt = wtable + (int64_t)g * max_logical;
+    for (int j = lo; j < hi; ++j) {
+      int ws = 0;
+      if (ng[j]) {
+        if (pos < wslots) {
+          items[base + pos] = make_int2(g * n_slots + table[(int64_t)g * max_logical + j],
+                                        g * wslots + pos);
+          ws = pos;
+        }
+        ++pos;
+      }
+      wt[j] = ws;
+    }
+    for (int j = n_pages + tid; j < max_logical; j += T) wt[j] = 0;
+    __syncthreads();
+    if (tid == T - 1) s_base = base + (s_sum[T - 1] < wslots ? s_sum[T - 1] : wslots);
+  }
   __syncthreads();
-  for (int off = 1; off < T; off <<= 1) {
-    const int add = tid >= off ? s_sum[tid - off] : 0;
-    __syncthreads();
-    s_sum[tid] += add;
-    __syncthreads();
-  }
-  int pos = s_sum[tid] - c;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int64_t at = (i % hkv) * max_logical + i / hkv;
-    if (need[at]) items[pos++] = ((i % hkv) * slots + table[at]) * page_elems;
-  }
-  if (tid == T - 1) *count = s_sum[T - 1];
+  if (tid == 0) *count = s_base;
 }
 
 __device__ __forceinline__ float4 lo4(uint4 a) {
@@ -130,7 +159,7 @@ __device__ __forceinline__ void widen(float* __restrict__ dst, const unsigned sh
 // Host -> window for every listed page-head: K and V (with_kv), and dK/dV
 // with grad_mode 1 (bf16 host gradients, widened to fp32) or 2 (fp32).
 __global__ void __launch_bounds__(256) fetch_kernel(
-    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    const int2* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
     bool with_kv, int kv_bytes, const char* __restrict__ hk, const char* __restrict__ hv,
     char* __restrict__ wk, char* __restrict__ wv, int grad_mode, const char* __restrict__ hdk,
     const char* __restrict__ hdv, float* __restrict__ wdk, float* __restrict__ wdv,
@@ -139,19 +168,20 @@ __global__ void __launch_bounds__(256) fetch_kernel(
   const int64_t per = (with_kv ? 2 * page_elems * kv_bytes : 0) +
                       (grad_mode ? 2 * page_elems * (grad_mode == 1 ? 2 : 4) : 0);
   int it = blockIdx.x;
-  int64_t e0 = it < n ? items[it] : 0;
+  int2 e0 = it < n ? items[it] : make_int2(0, 0);
   for (; it < n; it += gridDim.x) {
-    const int64_t e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : 0;
+    const int2 e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : make_int2(0, 0);
+    const int64_t eh = e0.x * page_elems, ew = e0.y * page_elems;  // tier, window
     if (with_kv) {
-      copy_bytes(wk + e0 * kv_bytes, hk + e0 * kv_bytes, page_elems * kv_bytes);
-      copy_bytes(wv + e0 * kv_bytes, hv + e0 * kv_bytes, page_elems * kv_bytes);
+      copy_bytes(wk + ew * kv_bytes, hk + eh * kv_bytes, page_elems * kv_bytes);
+      copy_bytes(wv + ew * kv_bytes, hv + eh * kv_bytes, page_elems * kv_bytes);
     }
     if (grad_mode == 1) {
-      widen(wdk + e0, (const unsigned short*)hdk + e0, page_elems);
-      widen(wdv + e0, (const unsigned short*)hdv + e0, page_elems);
+      widen(wdk + ew, (const unsigned short*)hdk + eh, page_elems);
+      widen(wdv + ew, (const unsigned short*)hdv + eh, page_elems);
     } else if (grad_mode == 2) {
-      copy_bytes((char*)(wdk + e0), hdk + e0 * 4, page_elems * 4);
-      copy_bytes((char*)(wdv + e0), hdv + e0 * 4, page_elems * 4);
+      copy_bytes((char*)(wdk + ew), hdk + eh * 4, page_elems * 4);
+      copy_bytes((char*)(wdv + ew), hdv + eh * 4, page_elems * 4);
     }
     e0 = e_next;
   }
@@ -163,14 +193,14 @@ __global__ void __launch_bounds__(256) fetch_kernel(
 // rather than the copy kernels' small one, which keeps the host link's
 // workgroups on host reads.
 __global__ void __launch_bounds__(256) window_grad_zero_kernel(
-    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    const int2* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
     float* __restrict__ wdk, float* __restrict__ wdv) {
   const int64_t per = page_elems / 4;  // float4 per page-head
   const int64_t total = (int64_t)*count * per;
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < total;
        u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t it = u / per, e = items[it] + (u - it * per) * 4;
+    const int64_t it = u / per, e = items[it].y * page_elems + (u - it * per) * 4;
     *reinterpret_cast<float4*>(wdk + e) = z;
     *reinterpret_cast<float4*>(wdv + e) = z;
   }
@@ -184,24 +214,25 @@ __device__ __forceinline__ unsigned to_bf16(float x) {
 // tier, or the staging of host accumulation, indexed alike), whole
 // page-heads per workgroup as in the fetch.
 __global__ void __launch_bounds__(256) writeback_kernel(
-    const int64_t* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
+    const int2* __restrict__ items, const int* __restrict__ count, int64_t page_elems,
     bool grad_bf16, char* __restrict__ hdk, char* __restrict__ hdv,
     const float* __restrict__ wdk, const float* __restrict__ wdv,
     unsigned long long* __restrict__ moved) {
   const int n = *count;
   int it = blockIdx.x;
-  int64_t e0 = it < n ? items[it] : 0;
+  int2 e0 = it < n ? items[it] : make_int2(0, 0);
   for (; it < n; it += gridDim.x) {
-    const int64_t e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : 0;
+    const int2 e_next = it + (int)gridDim.x < n ? items[it + gridDim.x] : make_int2(0, 0);
+    const int64_t eh = e0.x * page_elems, ew = e0.y * page_elems;  // tier, window
     if (!grad_bf16) {
-      copy_bytes(hdk + e0 * 4, (const char*)(wdk + e0), page_elems * 4);
-      copy_bytes(hdv + e0 * 4, (const char*)(wdv + e0), page_elems * 4);
+      copy_bytes(hdk + eh * 4, (const char*)(wdk + ew), page_elems * 4);
+      copy_bytes(hdv + eh * 4, (const char*)(wdv + ew), page_elems * 4);
     } else {
-      uint4* dk = reinterpret_cast<uint4*>(hdk + e0 * 2);
-      uint4* dv = reinterpret_cast<uint4*>(hdv + e0 * 2);
+      uint4* dk = reinterpret_cast<uint4*>(hdk + eh * 2);
+      uint4* dv = reinterpret_cast<uint4*>(hdv + eh * 2);
       for (int64_t i = threadIdx.x; i < page_elems / 8; i += blockDim.x) {
-        const float4* a = reinterpret_cast<const float4*>(wdk + e0 + 8 * i);
-        const float4* b = reinterpret_cast<const float4*>(wdv + e0 + 8 * i);
+        const float4* a = reinterpret_cast<const float4*>(wdk + ew + 8 * i);
+        const float4* b = reinterpret_cast<const float4*>(wdv + ew + 8 * i);
         const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
         dk[i] = make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
                            to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
@@ -268,15 +299,16 @@ namespace {
 
 struct WindowList {
   const uint8_t* need;
-  int64_t* items;
+  int2* items;
   int* count;
 };
 
 // The page map and list buffer the window's last prefetch built.
 WindowList window_list(const pkv_pool* p, int window) {
   const int64_t nw = need_words(p);
+  const int64_t ni = (int64_t)p->desc.n_kv_heads * p->window_slots;
   const int b = window * 2 + p->list_gen[window];
-  return {p->d_need + b * nw, p->d_items + b * nw, p->d_count + b};
+  return {p->d_need + b * nw, p->d_items + b * ni, p->d_count + b};
 }
 
 int64_t pages_of(const pkv_pool* p, int layer) {
@@ -291,7 +323,7 @@ hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStrea
   const int32_t* table = p->d_table + (int64_t)layer * need_words(p);
   hipLaunchKernelGGL(need_compact_kernel, dim3(1), dim3(1024), 0, s, L.need, table,
                      d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)pages_of(p, layer),
-                     (int64_t)d.page_size * d.head_dim, L.items, L.count);
+                     p->window_slots, L.items, L.count, p->d_wtable + window * need_words(p));
   return hipGetLastError();
 }
 
@@ -305,10 +337,10 @@ hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
   hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
                      (int64_t)d.page_size * d.head_dim, true, p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
-                     (char*)p->d_k + window * p->layer_elems * p->kv_bytes,
-                     (char*)p->d_v + window * p->layer_elems * p->kv_bytes, grad_mode,
+                     (char*)p->d_k + window * p->dev_elems * p->kv_bytes,
+                     (char*)p->d_v + window * p->dev_elems * p->kv_bytes, grad_mode,
                      (const char*)p->m_dk[layer], (const char*)p->m_dv[layer],
-                     p->d_dk + window * p->layer_elems, p->d_dv + window * p->layer_elems,
+                     p->d_dk + window * p->dev_elems, p->d_dv + window * p->dev_elems,
                      p->d_moved);
   return hipGetLastError();
 }
@@ -318,8 +350,8 @@ hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hip
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
   hipLaunchKernelGGL(window_grad_zero_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count,
-                     (int64_t)d.page_size * d.head_dim, p->d_dk + window * p->layer_elems,
-                     p->d_dv + window * p->layer_elems);
+                     (int64_t)d.page_size * d.head_dim, p->d_dk + window * p->dev_elems,
+                     p->d_dv + window * p->dev_elems);
   return hipGetLastError();
 }
 
@@ -334,8 +366,8 @@ hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipS
   hipLaunchKernelGGL(writeback_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
                      (int64_t)d.page_size * d.head_dim, d.host_grad_dtype == PKV_BF16,
                      (char*)dst_dk, (char*)dst_dv,
-                     (const float*)(p->d_dk + window * p->layer_elems),
-                     (const float*)(p->d_dv + window * p->layer_elems), p->d_moved + 1);
+                     (const float*)(p->d_dk + window * p->dev_elems),
+                     (const float*)(p->d_dv + window * p->dev_elems), p->d_moved + 1);
   return hipGetLastError();
 }
 

@@ -52,13 +52,27 @@ pkv_status pool_hip_fail(hipError_t e, const char* what) { return hip_fail(e, wh
 
 LayerDev layer_view(pkv_pool* p, int layer) {
   LayerDev L;
-  const int64_t kv_stride = p->layer_elems * p->kv_bytes;
-  const int64_t gr_stride = p->layer_elems;
-  const int wl = p->desc.host_tier ? p->window_of(layer) : layer;
-  L.k = (char*)p->d_k + wl * kv_stride;
-  L.v = (char*)p->d_v + wl * kv_stride;
-  L.dk = p->d_dk + wl * gr_stride;
-  L.dv = p->d_dv + wl * gr_stride;
+  const pkv_pool_desc& d = p->desc;
+  const int64_t tab_stride = (int64_t)d.n_kv_heads * d.max_logical_pages;
+  L.reps = p->d_reps + (int64_t)layer * d.n_kv_heads * d.n_slots * d.head_dim;
+  // host tier: the HBM window that holds the layer, reached through the
+  // window's table (logical page -> window slot)
+  const int64_t wl = d.host_tier ? p->window_of(layer) : layer;
+  L.k = (char*)p->d_k + wl * p->dev_elems * p->kv_bytes;
+  L.v = (char*)p->d_v + wl * p->dev_elems * p->kv_bytes;
+  L.dk = p->d_dk + wl * p->dev_elems;
+  L.dv = p->d_dv + wl * p->dev_elems;
+  L.table = (d.host_tier ? p->d_wtable : p->d_table) + wl * tab_stride;
+  return L;
+}
+
+LayerDev store_view(pkv_pool* p, int layer) {
+  if (!p->desc.host_tier) return layer_view(p, layer);
+  LayerDev L;
+  L.k = p->m_k[layer];
+  L.v = p->m_v[layer];
+  L.dk = (float*)p->m_dk[layer];
+  L.dv = (float*)p->m_dv[layer];
   L.reps = p->d_reps + (int64_t)layer * p->desc.n_kv_heads * p->desc.n_slots * p->desc.head_dim;
   L.table = p->d_table + (int64_t)layer * p->desc.n_kv_heads * p->desc.max_logical_pages;
   return L;
@@ -71,6 +85,12 @@ Geom geom(const pkv_pool* p) {
   g.page = p->desc.page_size;
   g.slots = p->desc.n_slots;
   g.max_logical = p->desc.max_logical_pages;
+  return g;
+}
+
+Geom compute_geom(const pkv_pool* p) {
+  Geom g = geom(p);
+  if (p->desc.host_tier) g.slots = p->window_slots;
   return g;
 }
 
@@ -125,6 +145,8 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
     return fail(PKV_EINVAL, "pkv_pool_create: host_grad_accumulate must be 0 or 1");
   if (d.host_grad_accumulate && !d.host_tier)
     return fail(PKV_EINVAL, "pkv_pool_create: host_grad_accumulate needs host_tier");
+  if (d.window_slots < 0 || (d.window_slots && !d.host_tier))
+    return fail(PKV_EINVAL, "pkv_pool_create: window_slots must be 0, or >= 1 with host_tier");
 
   pkv_pool* p = new (std::nothrow) pkv_pool();
   if (!p) return fail(PKV_ENOMEM, "pkv_pool_create: out of host memory");
@@ -132,6 +154,11 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
   p->kv_bytes = d.kv_dtype == PKV_BF16 ? 2 : 4;
   p->accumulate = d.host_grad_accumulate != 0;
   p->layer_elems = (int64_t)d.n_kv_heads * d.n_slots * d.page_size * d.head_dim;
+  p->window_slots = d.window_slots > 0 && d.window_slots < d.max_logical_pages
+                        ? d.window_slots : d.max_logical_pages;
+  p->dev_elems = d.host_tier
+                     ? (int64_t)d.n_kv_heads * p->window_slots * d.page_size * d.head_dim
+                     : p->layer_elems;
   p->length.assign(d.n_layers, 0);
   p->h_table.resize((size_t)d.n_layers * d.n_kv_heads * d.max_logical_pages);
   for (int l = 0; l < d.n_layers; ++l)
@@ -264,7 +291,7 @@ static AttnCall make_call(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t
   AttnCall c;
   std::memset(&c, 0, sizeof c);
   c.L = layer_view(pool, layer);
-  c.g = geom(pool);
+  c.g = compute_geom(pool);
   c.hq = hq;
   c.q_pos0 = q_pos0;
   c.n_q = (int)n_q;
@@ -278,6 +305,74 @@ static AttnCall make_call(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t
   return c;
 }
 
+}  // extern "C"
+
+namespace pkv {
+
+// Scratch bytes of one backward call; *plan_off: where the dK/dV work list
+// starts in it.
+int64_t bwd_scratch_bytes(pkv_pool* pool, int64_t q_pos0, int64_t n_q, int32_t n_q_heads,
+                          const pkv_sel* sel, int64_t* plan_off) {
+  // D and lse2 ([hq][n_q] fp32 each), then the sparse dK/dV work list
+  const int64_t dl_bytes = ((2 * (int64_t)n_q_heads * n_q * (int64_t)sizeof(float) + 255) / 256) * 256;
+  *plan_off = dl_bytes;
+  if (!sel || pool->desc.kv_dtype != PKV_BF16) return dl_bytes;
+  return dl_bytes + dkdv_plan_layout(geom(pool), n_q_heads, q_pos0, (int)n_q, sel->stride).bytes;
+}
+
+// The backward behind pkv_attn_bwd (scratch == nullptr: the pool's own,
+// grown on demand) and pkv_attn_bwd_noalloc (scratch: scratch_cap bytes the
+// caller provides; a larger need is PKV_ECAPACITY).
+pkv_status attn_bwd_impl(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                         int32_t n_q_heads, float scale, const void* q, const void* o,
+                         const void* dout, const float* lse, const pkv_sel* sel, float* dq,
+                         hipStream_t stream, void* scratch, int64_t scratch_cap, const char* who) {
+  pkv_status st = check_attn(pool, layer, q_pos0, n_q, n_q_heads, who);
+  if (st != PKV_OK) return st;
+  if (n_q == 0) return PKV_OK;
+  if (!q || !o || !dout || !lse || !dq) return fail(PKV_EINVAL, "%s: null q/o/dout/lse/dq", who);
+  if ((st = check_sel(pool, sel, n_q, who)) != PKV_OK) return st;
+  if (cdiv(n_q, pool->desc.page_size) > 1024)
+    return fail(PKV_EUNSUPPORTED, "%s: chunks of more than 1024 pages", who);
+  int64_t plan_off = 0;
+  const int64_t need = bwd_scratch_bytes(pool, q_pos0, n_q, n_q_heads, sel, &plan_off);
+  if (scratch) {
+    // caller-provided scratch: nothing may be allocated, and kernel timing
+    // creates events
+    if (kernel_timing_on())
+      return fail(PKV_ESTATE, "%s: not available while kernel timing is on", who);
+    if (need > scratch_cap)
+      return fail(PKV_ECAPACITY, "%s: the chunk needs %lld bytes of scratch, at most %lld",
+                  who, (long long)need, (long long)scratch_cap);
+  } else {
+    if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes, need)) != PKV_OK) return st;
+    scratch = pool->d_delta;
+  }
+  if ((st = pool_before_compute(pool, layer, q_pos0 + n_q, stream, true)) != PKV_OK) return st;
+  AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
+  c.q = q;
+  c.o = o;
+  c.dout = dout;
+  c.lse_in = lse;
+  c.dq = dq;
+  c.delta = (float*)scratch;
+  c.lse2 = pool->desc.kv_dtype == PKV_BF16 ? c.delta + (int64_t)n_q_heads * n_q : nullptr;
+  if (sel && pool->desc.kv_dtype == PKV_BF16) {
+    DkvPlan pl = dkdv_plan_layout(geom(pool), n_q_heads, q_pos0, (int)n_q, sel->stride);
+    pl.base = reinterpret_cast<int*>((char*)scratch + plan_off);
+    c.plan = pl;
+  }
+  hipError_t e = pool->desc.kv_dtype == PKV_BF16
+                     ? launch_bwd_bf16(c, stream, pool->s_aux, pool->ev_fork, pool->ev_join)
+                     : launch_bwd_f32(c, stream);
+  if (e != hipSuccess) return fail(PKV_EHIP, "%s: launch: %s", who, hipGetErrorString(e));
+  return pool_after_compute(pool, layer, stream);
+}
+
+}  // namespace pkv
+
+extern "C" {
+
 pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
                         int32_t n_q_heads, float scale, const void* q, const pkv_sel* sel,
                         void* o, float* lse, hipStream_t stream) {
@@ -286,7 +381,7 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   if (n_q == 0) return PKV_OK;
   if (!q || !o || !lse) return fail(PKV_EINVAL, "pkv_attn_fwd: null q/o/lse");
   if ((st = check_sel(pool, sel, n_q, "pkv_attn_fwd")) != PKV_OK) return st;
-  if ((st = pool_before_compute(pool, layer, stream, false)) != PKV_OK) return st;
+  if ((st = pool_before_compute(pool, layer, q_pos0 + n_q, stream, false)) != PKV_OK) return st;
   AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
   c.q = q;
   c.o_out = o;
@@ -300,36 +395,8 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
                         int32_t n_q_heads, float scale, const void* q, const void* o,
                         const void* dout, const float* lse, const pkv_sel* sel, float* dq,
                         hipStream_t stream) {
-  pkv_status st = check_attn(pool, layer, q_pos0, n_q, n_q_heads, "pkv_attn_bwd");
-  if (st != PKV_OK) return st;
-  if (n_q == 0) return PKV_OK;
-  if (!q || !o || !dout || !lse || !dq) return fail(PKV_EINVAL, "pkv_attn_bwd: null q/o/dout/lse/dq");
-  if ((st = check_sel(pool, sel, n_q, "pkv_attn_bwd")) != PKV_OK) return st;
-  if (cdiv(n_q, pool->desc.page_size) > 1024)
-    return fail(PKV_EUNSUPPORTED, "pkv_attn_bwd: chunks of more than 1024 pages");
-  // scratch: D and lse2 ([hq][n_q] fp32 each), then the sparse dK/dV work list
-  const int64_t dl_bytes = ((2 * (int64_t)n_q_heads * n_q * (int64_t)sizeof(float) + 255) / 256) * 256;
-  const bool plan = sel && pool->desc.kv_dtype == PKV_BF16;
-  DkvPlan pl{};
-  if (plan) pl = dkdv_plan_layout(geom(pool), n_q_heads, q_pos0, (int)n_q, sel->stride);
-  if ((st = ensure_scratch(&pool->d_delta, &pool->delta_bytes, dl_bytes + pl.bytes)) != PKV_OK)
-    return st;
-  if ((st = pool_before_compute(pool, layer, stream, true)) != PKV_OK) return st;
-  AttnCall c = make_call(pool, layer, q_pos0, n_q, n_q_heads, scale, sel);
-  c.q = q;
-  c.o = o;
-  c.dout = dout;
-  c.lse_in = lse;
-  c.dq = dq;
-  c.delta = (float*)pool->d_delta;
-  c.lse2 = pool->desc.kv_dtype == PKV_BF16 ? c.delta + (int64_t)n_q_heads * n_q : nullptr;
-  if (plan) {
-    pl.base = reinterpret_cast<int*>((char*)pool->d_delta + dl_bytes);
-    c.plan = pl;
-  }
-  hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_bwd_bf16(c, stream, pool->s_aux, pool->ev_fork, pool->ev_join) : launch_bwd_f32(c, stream);
-  if (e != hipSuccess) return hip_fail(e, "pkv_attn_bwd: launch");
-  return pool_after_compute(pool, layer, stream);
+  return attn_bwd_impl(pool, layer, q_pos0, n_q, n_q_heads, scale, q, o, dout, lse, sel, dq,
+                       stream, nullptr, 0, "pkv_attn_bwd");
 }
 
 pkv_status pkv_measure_gather(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
@@ -384,7 +451,7 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
   if ((st = ensure_scratch(&pool->d_select, &pool->select_bytes,
                            select_scratch_floats(g, q_pos0, (int)n_q, n_sink, n_local) * 4)) != PKV_OK)
     return st;
-  hipError_t e = launch_select(layer_view(pool, layer), g, pool->desc.kv_dtype == PKV_BF16,
+  hipError_t e = launch_select(store_view(pool, layer), g, pool->desc.kv_dtype == PKV_BF16,
                                n_q_heads, q_pos0, (int)n_q, q, top_k, n_sink, n_local, sel_pages,
                                sel_count, sel_stride, (float*)pool->d_select, stream);
   if (e != hipSuccess) return hip_fail(e, "pkv_select_topk_pages: launch");

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <sched.h>
 
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <exception>
@@ -69,15 +70,18 @@ pkv_status pool_allocate(pkv_pool* p) {
   const pkv_pool_desc& d = p->desc;
   const int copies = d.host_tier ? pkv_pool::kWindow : d.n_layers;
   pkv_status st;
-  const int64_t kvb = p->layer_elems * p->kv_bytes * copies;
-  const int64_t grb = p->layer_elems * 4 * copies;
+  const int64_t kvb = p->dev_elems * p->kv_bytes * copies;
+  const int64_t grb = p->dev_elems * 4 * copies;
   const int64_t repb = (int64_t)d.n_layers * d.n_kv_heads * d.n_slots * d.head_dim * 4;
   const int64_t tabb = (int64_t)d.n_layers * d.n_kv_heads * d.max_logical_pages * 4;
-  // page maps and lists: two buffers per window
+  // host tier: page maps and page-head lists (two buffers per window), and
+  // the windows' tables
+  const int64_t wtabb = d.host_tier ? (int64_t)pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages * 4 : 0;
   const int64_t needb = d.host_tier ? (int64_t)2 * pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
-  const int64_t itemb = 8 * needb + 4 * 2 * pkv_pool::kWindow;
+  const int64_t itemb = d.host_tier ? (int64_t)8 * 2 * pkv_pool::kWindow * d.n_kv_heads * p->window_slots : 0;
+  const int64_t countb = 4 * 2 * pkv_pool::kWindow;
   if (d.host_tier && d.device_budget_bytes > 0 &&
-      2 * kvb + 2 * grb + repb + tabb + needb + itemb + 16 > d.device_budget_bytes)
+      2 * kvb + 2 * grb + repb + tabb + wtabb + needb + itemb + countb + 16 > d.device_budget_bytes)
     return pool_fail(PKV_ENOMEM, "host-tier window does not fit device_budget_bytes");
   if ((st = dev_alloc(p, &p->d_k, kvb, "device allocation of the K pool failed")) != PKV_OK) return st;
   if ((st = dev_alloc(p, &p->d_v, kvb, "device allocation of the V pool failed")) != PKV_OK) return st;
@@ -93,9 +97,10 @@ pkv_status pool_allocate(pkv_pool* p) {
       (e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming)) != hipSuccess)
     return pool_hip_fail(e, "hipEventCreate");
   if (d.host_tier) {
+    if ((st = dev_alloc(p, (void**)&p->d_wtable, wtabb, "device allocation of the window tables failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_need, needb, "device allocation of the window map failed")) != PKV_OK) return st;
-    if ((st = dev_alloc(p, (void**)&p->d_items, 8 * needb, "device allocation of the window list failed")) != PKV_OK) return st;
-    if ((st = dev_alloc(p, (void**)&p->d_count, 4 * 2 * pkv_pool::kWindow, "device allocation of the window list failed")) != PKV_OK) return st;
+    if ((st = dev_alloc(p, (void**)&p->d_items, itemb, "device allocation of the window list failed")) != PKV_OK) return st;
+    if ((st = dev_alloc(p, (void**)&p->d_count, countb, "device allocation of the window list failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_moved, 16, "device allocation of the copy counters failed")) != PKV_OK) return st;
     for (int w = 0; w < pkv_pool::kWindow; ++w) {
       if ((e = hipEventCreateWithFlags(&p->ev_compute[w], hipEventDisableTiming)) != hipSuccess)
@@ -169,8 +174,8 @@ pkv_status pool_release(pkv_pool* p) {
   for (int w = 0; w < pkv_pool::kWindow; ++w)
     for (void* x : {p->h_stage_dk[w], p->h_stage_dv[w], (void*)p->h_stage_need[w]})
       if (x) (void)hipHostFree(x);
-  void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_delta,
-                 p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved};
+  void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_wtable,
+                 p->d_delta, p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved};
   for (void* x : dev)
     if (x) (void)hipFree(x);
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
@@ -189,24 +194,20 @@ pkv_status pool_release(pkv_pool* p) {
   return st;
 }
 
-// The K/V/dK/dV bases a kernel should read or write for `layer`: the HBM
-// pool, or the device-visible mapping of the host tier.
-static LayerDev store_view(pkv_pool* p, int layer) {
-  LayerDev L = layer_view(p, layer);
-  if (p->desc.host_tier) {
-    L.k = p->m_k[layer];
-    L.v = p->m_v[layer];
-    L.dk = (float*)p->m_dk[layer];
-    L.dv = (float*)p->m_dv[layer];
-  }
-  return L;
-}
-
 pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, const void* k,
                        const void* v, hipStream_t s) {
   const LayerDev L = store_view(p, layer);
   const Geom g = geom(p);
-  hipError_t e = launch_append(L, g, p->kv_bytes, pos0, n_tok, k, v, s);
+  hipError_t e;
+  // A window's fetch may still be reading the partial last page that this
+  // append writes: order the append after it.  (The window does not get the
+  // new tokens; attention on them needs another prefetch, see
+  // pool_before_compute.)
+  const int w = p->window_of(layer);
+  if (p->desc.host_tier && p->window_layer[w] == layer && p->ready_recorded[w] &&
+      (e = hipStreamWaitEvent(s, p->ev_ready[w], 0)) != hipSuccess)
+    return pool_hip_fail(e, "pkv_append_kv: hipStreamWaitEvent (window fetch)");
+  e = launch_append(L, g, p->kv_bytes, pos0, n_tok, k, v, s);
   if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: append launch");
   const int64_t first = pos0 / g.page;
   const int64_t last = (pos0 + n_tok - 1) / g.page;
@@ -233,8 +234,8 @@ pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s) {
   const int w = p->window_of(layer);
   if (p->window_layer[w] == layer) {
     const LayerDev L = layer_view(p, layer);
-    if ((e = launch_fill_zero(L.dk, p->layer_elems * 4, s)) != hipSuccess ||
-        (e = launch_fill_zero(L.dv, p->layer_elems * 4, s)) != hipSuccess)
+    if ((e = launch_fill_zero(L.dk, p->dev_elems * 4, s)) != hipSuccess ||
+        (e = launch_fill_zero(L.dv, p->dev_elems * 4, s)) != hipSuccess)
       return pool_hip_fail(e, "pkv_grad_zero (window)");
   }
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return pool_hip_fail(e, "pkv_grad_zero: sync");
@@ -246,7 +247,7 @@ pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s)
   const int64_t n_tok = p->length[layer];
   hipError_t e;
   if (!p->desc.host_tier || what == PKV_REPS) {
-    e = launch_export(layer_view(p, layer), g, what, p->kv_bytes, n_tok, dst, s);
+    e = launch_export(store_view(p, layer), g, what, p->kv_bytes, n_tok, dst, s);
   } else {
     if ((e = hipDeviceSynchronize()) != hipSuccess) return pool_hip_fail(e, "pkv_read_pages: sync");
     const pkv_status st = pool_host_adds_wait(p);
@@ -273,11 +274,22 @@ static pkv_status zero_window_grads(pkv_pool* p, int layer, int w, hipStream_t s
   return PKV_OK;
 }
 
-pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s, bool grads) {
+pkv_status pool_before_compute(pkv_pool* p, int layer, int64_t q_end, hipStream_t s, bool grads) {
   if (!p->desc.host_tier) return PKV_OK;
   const int w = p->window_of(layer);
   if (p->window_layer[w] != layer)
     return pool_fail(PKV_ESTATE, "layer is not in the HBM window: call pkv_prefetch_pages first");
+  if (q_end > p->window_keys[w])
+    return pool_fail(PKV_ESTATE,
+                     "queries reach past the keys the window's prefetch covered (tokens appended "
+                     "after it, or a shorter prefix): call pkv_prefetch_pages again");
+  // the backward adds into the window's gradients: they must be this
+  // visit's (fetched, or zeroed for host adds) and not yet handed to a
+  // writeback that ends the visit
+  if (grads && !p->window_grads[w])
+    return pool_fail(PKV_ESTATE,
+                     "attention backward on a window whose gradients were not prefetched "
+                     "(with_grads) or were already written back");
   if (p->ready_recorded[w]) {
     hipError_t e = hipStreamWaitEvent(s, p->ev_ready[w], 0);
     if (e != hipSuccess) return pool_hip_fail(e, "hipStreamWaitEvent (window ready)");
@@ -299,6 +311,19 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   const int w = p->window_of(layer);
   const pkv_pool_desc& d = p->desc;
   hipError_t e;
+  // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every appended key)
+  const int64_t n_avail = n_keys > 0 && n_keys < p->length[layer] ? n_keys : p->length[layer];
+  const int64_t n_pages = (n_avail + d.page_size - 1) / d.page_size;
+  // the page-heads one KV head can need must fit the window's slots
+  int64_t bound = n_pages;
+  if (sel && (int64_t)sel->n_qpages * sel->stride < bound) bound = (int64_t)sel->n_qpages * sel->stride;
+  if (bound > p->window_slots) {
+    char msg[200];
+    snprintf(msg, sizeof msg,
+             "prefetch could need %lld pages per KV head, the window holds %d (window_slots)",
+             (long long)bound, p->window_slots);
+    return pool_fail(PKV_ECAPACITY, msg);
+  }
   // K/V of the window are free once the attention calls on its last layer ran
   if (p->compute_recorded[w]) {
     if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
@@ -313,15 +338,13 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   p->list_gen[w] = b;
   const int64_t nw = need_words(p);
   uint8_t* need = p->d_need + (int64_t)(w * 2 + b) * nw;
-  // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every appended key)
-  const int64_t n_avail = n_keys > 0 && n_keys < p->length[layer] ? n_keys : p->length[layer];
-  const int64_t n_pages = (n_avail + d.page_size - 1) / d.page_size;
   if ((e = launch_need_clear(need, nw, cs)) != hipSuccess ||
       (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess ||
       (e = launch_window_list(p, layer, w, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");
   p->window_layer[w] = layer;
   p->window_grads[w] = with_grads;
+  p->window_keys[w] = n_avail;
   // Gradients fetched into HBM (no host accumulation): one launch for K/V and
   // gradients after the window's last writeback has read its gradients.
   // Fetching K/V before that wait and the gradients after it ran the K/V

@@ -14,18 +14,26 @@
 struct pkv_pool {
   pkv_pool_desc desc{};
   int kv_bytes = 2;          // bytes per K/V element
-  int64_t layer_elems = 0;   // Hkv * slots * P * d
+  int64_t layer_elems = 0;   // Hkv * n_slots * P * d: one layer of the pool (host tier: of the tier)
+  // Host tier: HBM slots per KV head in each window (desc.window_slots, or a
+  // whole layer's max_logical_pages), and the elements of one device copy of
+  // K, V, dK or dV (a window with a host tier, a layer without)
+  int window_slots = 0;
+  int64_t dev_elems = 0;
   std::vector<int64_t> length;    // appended tokens per layer
   std::vector<int32_t> h_table;   // [layers][Hkv][max_logical], host mirror
 
-  // Device buffers.  Without a host tier: n_layers copies of K, V, dK, dV.
-  // With a host tier: kWindow copies (the HBM window).
+  // Device buffers.  Without a host tier: n_layers copies of K, V, dK, dV
+  // ([Hkv][n_slots][P][d] each).  With a host tier: kWindow windows of
+  // [Hkv][window_slots][P][d] each, a window's pages reached through its
+  // table d_wtable[w] ([Hkv][max_logical]: logical page -> window slot).
   void* d_k = nullptr;
   void* d_v = nullptr;
   float* d_dk = nullptr;
   float* d_dv = nullptr;
   float* d_reps = nullptr;        // [layers][Hkv][slots][d]
   int32_t* d_table = nullptr;     // [layers][Hkv][max_logical]
+  int32_t* d_wtable = nullptr;    // host tier: [kWindow][Hkv][max_logical]
   void* d_delta = nullptr;        // attn_bwd scratch
   // attn_bwd (bf16) runs dQ and dK/dV side by side: dK/dV on this stream,
   // forked from and joined back to the caller's stream with the two events
@@ -43,6 +51,10 @@ struct pkv_pool {
   std::vector<void*> m_k, m_v, m_dk, m_dv;      // device-visible aliases
   int window_layer[kWindow] = {-1, -1};
   bool window_grads[kWindow] = {false, false};  // grads of the needed pages were fetched
+  // keys of the window's layer present when its last prefetch ran (a prefix
+  // prefetch: the keys it names): attention needs queries below this, since
+  // tokens appended later are not in the window
+  int64_t window_keys[kWindow] = {0, 0};
   hipEvent_t ev_compute[kWindow] = {nullptr, nullptr};  // after the last attention call
   hipEvent_t ev_ready[kWindow] = {nullptr, nullptr};    // after the last prefetch
   hipEvent_t ev_wb[kWindow] = {nullptr, nullptr};       // after the last grad writeback
@@ -54,7 +66,9 @@ struct pkv_pool {
   // buffer list_gen[w]; ev_list[w][b] is recorded after the writeback that
   // read buffer b.
   uint8_t* d_need = nullptr;      // [kWindow][2][Hkv][max_logical] page-heads held by the window
-  int64_t* d_items = nullptr;     // [kWindow][2][Hkv * max_logical] their element offsets, listed
+  // [kWindow][2][Hkv * window_slots] the listed page-heads: (tier page-head
+  // g * n_slots + slot, window page-head g * window_slots + window slot)
+  int2* d_items = nullptr;
   int* d_count = nullptr;         // [kWindow][2] list lengths
   int list_gen[kWindow] = {0, 0};
   hipEvent_t ev_list[kWindow][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -86,7 +100,13 @@ namespace pkv {
 
 pkv_status pool_fail(pkv_status st, const char* msg);
 pkv_status pool_hip_fail(hipError_t e, const char* what);
+// What the attention kernels read and write for `layer`: its HBM pool, or
+// with a host tier the window holding it (window table, window slots).
 LayerDev layer_view(pkv_pool* p, int layer);
+Geom compute_geom(const pkv_pool* p);
+// The layer's own store: its HBM pool, or the device-mapped host tier; page
+// table and representatives of the layer (slots = n_slots).
+LayerDev store_view(pkv_pool* p, int layer);
 Geom geom(const pkv_pool* p);
 pkv_status ensure_scratch(void** buf, int64_t* have, int64_t need);
 
@@ -96,12 +116,19 @@ pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, cons
                        const void* v, hipStream_t s);
 pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_read(pkv_pool* p, int layer, int what, void* dst, hipStream_t s);
-pkv_status pool_before_compute(pkv_pool* p, int layer, hipStream_t s, bool grads);
+pkv_status pool_before_compute(pkv_pool* p, int layer, int64_t q_end, hipStream_t s, bool grads);
 pkv_status pool_after_compute(pkv_pool* p, int layer, hipStream_t s);
 pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_keys, bool with_grads,
                          hipStream_t copy_stream, hipEvent_t ready);
 pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t copy_stream, hipEvent_t done);
 pkv_status pool_copy_stats(pkv_pool* p, int64_t* fetched, int64_t* written);
+
+// pkv_api.cpp: the attention backward with the pool's own scratch (scratch ==
+// nullptr) or scratch_cap bytes of the caller's (no allocation)
+pkv_status attn_bwd_impl(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                         int32_t n_q_heads, float scale, const void* q, const void* o,
+                         const void* dout, const float* lse, const pkv_sel* sel, float* dq,
+                         hipStream_t stream, void* scratch, int64_t scratch_cap, const char* who);
 
 // offload.hip
 hipError_t launch_need_clear(uint8_t* need, int64_t n, hipStream_t s);

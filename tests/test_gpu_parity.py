@@ -37,15 +37,36 @@ def _check(cfg, got, ref, tol):
     return errs
 
 
+def _gpu_sels(cfg, got):
+    """The GPU's selections in the oracle's format (per chunk, per query page,
+    per KV head: ascending page ids)."""
+    out = []
+    for c in range(cfg.n_chunks):
+        pages, count = got["sel"][c]
+        out.append([[pages[i, g, :count[i, g]].astype(np.int64) for g in range(cfg.hkv)]
+                    for i in range(pages.shape[0])])
+    return out
+
+
 def _check_sel(cfg, f, got, ref, sparse):
+    """Selections of every chunk against the oracle's fp32 scoring, equal
+    except for candidates within 1e-5 of the K-th score.  Returns the oracle
+    result to compare values with: `ref` when the selections are equal, else
+    the oracle run on the GPU's own selections (the gap rule makes each of
+    them a correct selection; the attention given a selection is exact)."""
+    n_diff = 0
     for c in range(cfg.n_chunks):
         q_pos0, n = cfg.chunk_range(c)
         _, scores = oracle.select_pages(f.q[q_pos0:q_pos0 + n], f.k, q_pos0, cfg.page, cfg.hkv,
                                         sparse.top_k, sparse.n_sink, sparse.n_local,
                                         return_scores=True)
-        nd = compare_selection(sel_lists(got["sel"][c]), ref["sel"][c], scores, sparse.top_k)
-        if nd:
-            pytest.skip(f"selection differs inside the 1e-5 score gap in chunk {c}")
+        n_diff += compare_selection(sel_lists(got["sel"][c]), ref["sel"][c], scores, sparse.top_k)
+    if n_diff == 0:
+        return ref
+    print(f"{cfg.name}: {n_diff} lists differ inside the 1e-5 score gap; values checked on "
+          "the GPU's selections", flush=True)
+    return oracle.run_chunks(f.q, f.k, f.v, f.do, cfg.chunk, cfg.scale, cfg.page,
+                             sels=_gpu_sels(cfg, got))
 
 
 def test_tiny_f32_dense():
@@ -63,7 +84,7 @@ def test_tiny_f32_sparse():
     w = Workload(cfg)
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
-    _check_sel(cfg, f, got, ref, sp)
+    ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["f32"])
 
 
@@ -91,7 +112,7 @@ def test_bf16_qwen_sparse():
     w = Workload(cfg)
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
-    _check_sel(cfg, f, got, ref, sp)
+    ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["bf16"])
 
 
@@ -125,7 +146,7 @@ def test_bf16_qwen_sparse_partial_page_tail():
     w = Workload(cfg)
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
-    _check_sel(cfg, f, got, ref, sp)
+    ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["bf16"])
 
 
@@ -179,7 +200,7 @@ def test_bf16_other_shapes(hq, hkv, page, sparse_k):
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
     if sp is not None:
-        _check_sel(cfg, f, got, ref, sp)
+        ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["bf16"])
 
 
@@ -195,7 +216,7 @@ def test_bf16_sparse_chunk_over_64_query_pages():
     w = Workload(cfg)
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
-    _check_sel(cfg, f, got, ref, sp)
+    ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL["bf16"])
 
 
@@ -324,6 +345,60 @@ def test_one_token_last_chunk(name, sparse_k):
     got = run_layer(cfg, w, sparse=sp)
     f, ref = _oracle_for(cfg, w, sp)
     if sp is not None:
-        _check_sel(cfg, f, got, ref, sp)
+        ref = _check_sel(cfg, f, got, ref, sp)
     _check(cfg, got, ref, TOL[cfg.dtype])
+    got["pool"].close()
+
+
+@pytest.mark.parametrize("top_k", [1, 2, 4, 7])
+def test_bf16_selection_ties_go_to_the_lower_page(top_k):
+    """Exact ties on the GPU.  Key pages 4.. are copies of pages 1, 2 or 3, so
+    the fp32 representatives of a template's copies are bit-identical (the
+    same keys summed in the same order) and so are their scores: the budget
+    cuts through groups of equal scores, where only the tie rule (the lower
+    page index first) decides.  The scores of different templates lie at
+    least 8e-5 apart on these seeded inputs (checked below on the oracle), far
+    beyond any fp32 rounding difference, so the GPU's lists must equal the
+    oracle's (fp32 scoring, ties to the lower page) exactly, with no gap
+    allowance; then O, LSE, dQ, dK, dV against the oracle on that
+    selection."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    from synthetic.gen import ChunkInputs
+    cfg = mini_config("qwen_256k_topk", n_ctx=3072, chunk=1024, top_k=top_k)
+    w = Workload(cfg)
+    f = w.full()
+    P = cfg.page
+    k = f.k.copy()
+    for p in range(4, cfg.n_pages):
+        t = 1 + (5 * p) % 3
+        k[p * P:(p + 1) * P] = k[t * P:(t + 1) * P]
+    chunks = []
+    for c in range(cfg.n_chunks):
+        q_pos0, n = cfg.chunk_range(c)
+        sl = slice(q_pos0, q_pos0 + n)
+        chunks.append(ChunkInputs(q_pos0, f.q[sl], k[sl], f.v[sl], f.do[sl]))
+    sp = Sparse(top_k=top_k)
+    got = run_layer(cfg, w, sparse=sp, chunks=chunks)
+    ties_cut = 0
+    for c in range(cfg.n_chunks):
+        q_pos0, n = cfg.chunk_range(c)
+        ref_sel = oracle.select_pages(f.q[q_pos0:q_pos0 + n], k, q_pos0, P, cfg.hkv, top_k,
+                                      sp.n_sink, sp.n_local, score_dtype=np.float32)
+        kbar = oracle.key_page_means(k[:q_pos0 + n], P).astype(np.float32)
+        qbar = oracle.query_page_means(f.q[q_pos0:q_pos0 + n], P, cfg.hkv).astype(np.float32)
+        for il, row in enumerate(sel_lists(got["sel"][c])):
+            i = q_pos0 // P + il
+            for g, lst in enumerate(row):
+                assert lst == ref_sel[il][g].tolist(), (c, il, g, lst, ref_sel[il][g].tolist())
+                cand = np.arange(sp.n_sink, i - sp.n_local + 1)
+                if cand.size <= top_k:
+                    continue
+                s = np.sort((kbar[cand, g] * qbar[il, g][None]).sum(axis=1, dtype=np.float32))
+                u = np.unique(s)
+                assert u.size < 2 or np.diff(u).min() > 1e-5  # distinct scores well apart
+                ties_cut += bool(s[::-1][top_k - 1] == s[::-1][top_k])
+    assert ties_cut > 0, "no list had its budget cut through a tie"
+    print(f"top_k {top_k}: {ties_cut} lists cut through a tie", flush=True)
+    ref = oracle.run_chunks(f.q, k, f.v, f.do, cfg.chunk, cfg.scale, P, sels=_gpu_sels(cfg, got))
+    _check(cfg, got, ref, TOL["bf16"])
     got["pool"].close()
