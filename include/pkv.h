@@ -229,6 +229,27 @@ pkv_status pkv_attn_bwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
                         const void* dout, const float* lse, const pkv_sel* sel, float* dq,
                         hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward as pkv_attn_bwd (same arguments, checks, kernels and results), but
+ * its scratch (D, the base-2 log-sum-exp and the top-K dK/dV work list) is a
+ * fixed 16 MiB device array of the library instead of pool memory grown with
+ * hipMalloc; the call allocates nothing.  Each GPU holds its own array (on
+ * the current device, which must be the pool's) from the first call until
+ * the process ends.  A chunk whose scratch exceeds 16 MiB, 2 x n_q_heads x
+ * n_q x 4 bytes rounded up to 256 plus, with a top-K selection on a bf16
+ * pool, the work list (about 4 x Hkv x context pages x (1 + ceil(n_q / P /
+ * 32)) + 32 x (P / 128) x n_qpages x Hkv x stride bytes; 1.5 MB for chunks
+ * of 8192 tokens at a 1M-token context), returns PKV_ECAPACITY; while
+ * kernel timing is on it returns PKV_ESTATE.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * pools, other threads) race and must be ordered by the caller.  Nothing in
+ * the array needs to start at zero. */
+pkv_status pkv_attn_bwd_noalloc(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
+                                int32_t n_q_heads, float scale, const void* q, const void* o,
+                                const void* dout, const float* lse, const pkv_sel* sel,
+                                float* dq, hipStream_t stream);
+
 /* Page-level top-K selection for every query page of one chunk (de 2.D; nl
  * "Methodologie"; sciencestack Figure 5).  For query page i (absolute) and
  * KV head g:

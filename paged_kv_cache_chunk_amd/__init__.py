@@ -27,7 +27,7 @@ EXPORTS = (
     "pkv_prefetch_pages", "pkv_writeback_grads", "pkv_grad_zero", "pkv_read_pages",
     "pkv_pool_bytes", "pkv_last_error", "pkv_pool_reset", "pkv_kernel_timing",
     "pkv_kernel_times", "pkv_offload_bytes", "pkv_measure_gather", "pkv_measure_atomics",
-    "pkv_read_rows", "pkv_prefetch_prefix",
+    "pkv_read_rows", "pkv_prefetch_prefix", "pkv_attn_bwd_noalloc",
 )
 KERNEL_KINDS = ("append", "select", "fwd", "delta", "dq", "dkdv", "fetch", "writeback")
 
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
             "pkv_attn_fwd": [P, I32, I64, I64, I32, F, VP, ctypes.POINTER(pkv_sel), VP, VP, VP],
             "pkv_attn_bwd": [P, I32, I64, I64, I32, F, VP, VP, VP, VP,
                              ctypes.POINTER(pkv_sel), VP, VP],
+            "pkv_attn_bwd_noalloc": [P, I32, I64, I64, I32, F, VP, VP, VP, VP,
+                                     ctypes.POINTER(pkv_sel), VP, VP],
             "pkv_select_topk_pages": [P, I32, I64, I64, I32, VP, I32, I32, I32, VP, VP, I32, VP],
             "pkv_prefetch_pages": [P, I32, ctypes.POINTER(pkv_sel), I32, VP, VP],
             "pkv_prefetch_prefix": [P, I32, I64, I32, VP, VP],
@@ -206,6 +208,13 @@ def pkv_attn_bwd(pool: Pool, layer: int, q_pos0: int, q, o, dout, lse, dq, scale
     _check(lib().pkv_attn_bwd(pool.handle, layer, q_pos0, q.shape[0], q.shape[1], scale,
                               _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), _selp(sel), _ptr(dq),
                               _stream(stream)))
+
+
+def pkv_attn_bwd_noalloc(pool: Pool, layer: int, q_pos0: int, q, o, dout, lse, dq, scale: float,
+                         sel=None, stream=None) -> None:
+    _check(lib().pkv_attn_bwd_noalloc(pool.handle, layer, q_pos0, q.shape[0], q.shape[1], scale,
+                                      _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), _selp(sel),
+                                      _ptr(dq), _stream(stream)))
 
 
 def pkv_select_topk_pages(pool: Pool, layer: int, q_pos0: int, q, top_k: int, sel_pages,
