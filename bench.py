@@ -31,7 +31,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dq": 6, "dkdv": 8}  # x d x Hq per attended pair
+# x d x Hq per attended (query, key) pair.  Executed: what each kernel
+# computes (the dQ kernel recomputes S and dP, so the three kernels execute
+# 18 d per pair); algorithmic: the kernel's share of the 14 d a training step
+# needs (forward 4 d; backward 10 d = S 2 + dP 2 + dV 2 + dK 2 in the dK/dV
+# kernel, dQ 2 in the dQ kernel).
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "dq": 6, "dkdv": 8}
+KERNEL_FLOPS_ALGORITHMIC = {"fwd": 4, "dq": 2, "dkdv": 8}
 
 
 def log(*a):
@@ -39,11 +45,13 @@ def log(*a):
 
 
 def source_hash() -> str:
-    """Hash of the bf16 attention kernel sources and their compile flags: stored
-    counter readings only apply to the kernels they were taken on."""
+    """Hash of the bf16 attention and measurement kernel sources and their
+    compile flags: stored counter readings only apply to the kernels they were
+    taken on."""
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "paged_kv_cache_chunk_amd")
-    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "attn_bf16_*"))) + [os.path.join(pkg, "build.py")]:
+    for p in sorted(glob.glob(os.path.join(pkg, "csrc", "attn_bf16_*"))) + [
+            os.path.join(pkg, "csrc", "micro.hip"), os.path.join(pkg, "build.py")]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -164,8 +172,10 @@ def kernel_table(lb: LayerBench, ms_step: float, ktimes: dict, steps: int) -> di
             continue
         e = {"launches_per_step": n // steps, "avg_ms": tot / n, "ms_per_step": tot / steps}
         if k in KERNEL_FLOPS_PER_PAIR:
-            fl = KERNEL_FLOPS_PER_PAIR[k] * cfg.d * pairs  # pairs already x Hq
-            e["tflops"] = fl * steps / (tot * 1e-3) / 1e12
+            # pairs are already x Hq
+            e["tflops_executed"] = KERNEL_FLOPS_PER_PAIR[k] * cfg.d * pairs * steps / (tot * 1e-3) / 1e12
+            e["tflops_algorithmic"] = (KERNEL_FLOPS_ALGORITHMIC[k] * cfg.d * pairs * steps
+                                       / (tot * 1e-3) / 1e12)
         out[k] = e
     return out
 
@@ -260,13 +270,23 @@ def phase_rates(lb: "LayerBench", reps: int = 3) -> dict:
     atom_bytes = n_keys * cfg.hkv * cfg.d * 4 * 2 * a_reps
     pkv.pkv_grad_zero(lb.pool, 0)
     torch.cuda.synchronize()
-    return {"chunk": f"rows {q_pos0}..{q_pos0 + n_q - 1}",
-            "gather": {"tile_bytes": gather_bytes, "ms": round(t_g, 3),
-                       "gb_per_s": round(gather_bytes / t_g / 1e6, 1),
-                       "fwd_ms_same_chunk": round(t_f, 3),
-                       "fwd_tile_gb_per_s": round(gather_bytes / t_f / 1e6, 1)},
-            "atomics": {"adds": n_keys * cfg.hkv * cfg.d * 2 * a_reps, "ms": round(t_a, 3),
-                        "gb_per_s": round(atom_bytes / t_a / 1e6, 1)}}
+    out = {"chunk": f"rows {q_pos0}..{q_pos0 + n_q - 1}",
+           "gather": {"tile_bytes": gather_bytes, "ms": round(t_g, 3),
+                      "l2_to_lds_gb_per_s": round(gather_bytes / t_g / 1e6, 1),
+                      "fwd_ms_same_chunk": round(t_f, 3),
+                      "fwd_l2_to_lds_gb_per_s": round(gather_bytes / t_f / 1e6, 1)},
+           "atomics": {"adds": n_keys * cfg.hkv * cfg.d * 2 * a_reps, "ms": round(t_a, 3),
+                       "add_gb_per_s": round(atom_bytes / t_a / 1e6, 1),
+                       "add_bytes_frac_of_hbm_peak": round(atom_bytes / t_a / 1e6 / PEAK_HBM_GBS, 4)}}
+    # HBM bytes the two measurement kernels moved (rocprofv3 FETCH_SIZE /
+    # WRITE_SIZE, profiles/traffic.json), as a rate and a fraction of 8 TB/s
+    for phase, kern, t in (("gather", "gather", t_g), ("atomics", "atomics", t_a)):
+        tb = traffic_for(kern, cfg.name)
+        out[phase]["hbm_bytes"] = tb
+        if tb:
+            out[phase]["hbm_gb_per_s"] = round(tb / t / 1e6, 1)
+            out[phase]["hbm_frac_of_peak"] = round(tb / t / 1e6 / PEAK_HBM_GBS, 4)
+    return out
 
 
 def block_bench(n_ctx: int, chunk: int, top_k: int = 0) -> dict:
@@ -378,6 +398,42 @@ def cpu_baseline(lb: LayerBench, rows: int) -> dict:
             "sample": f"fp64 numpy oracle fwd+bwd of the last {rows} query rows x {cfg.hq} heads "
                       f"against all {N} keys ({sample_pairs} pairs/head of {total_pairs}); "
                       f"{dt:.1f}s, scaled by the pair share"}
+
+
+def cpu_baseline_topk(lb: LayerBench, rows: int) -> dict:
+    """The fp64 oracle on a bounded sample of the top-K workload: the
+    selection of the last chunk's query pages, then forward + backward of the
+    last `rows` query rows (all heads) restricted to it, timed on this host;
+    scaled to tokens/s of the whole workload by the share of attended pairs
+    the sample covers."""
+    import numpy as np
+    import oracle
+
+    cfg = lb.cfg
+    N = cfg.n_ctx
+    k = np.concatenate([ch["k"].float().cpu().numpy() for ch in lb.chunks])
+    v = np.concatenate([ch["v"].float().cpu().numpy() for ch in lb.chunks])
+    last = lb.chunks[-1]
+    q_all = last["q"].float().cpu().numpy()
+    q_pos0 = last["q_pos0"]
+    do = last["do"][-rows:].float().cpu().numpy()
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    sel = oracle.select_pages(q_all, k, q_pos0, cfg.page, cfg.hkv, cfg.top_k, cfg.n_sink,
+                              cfg.n_local, score_dtype=np.float32)
+    r0 = q_all.shape[0] - rows
+    sub = sel[r0 // cfg.page:]
+    oracle.attn_bwd(q_all[r0:], k, v, do, q_pos0 + r0, cfg.scale, cfg.page, sub)
+    dt = time.perf_counter() - t0
+    counts = np.array([[len(x) for x in row] for row in sub])
+    sample_pairs = sparse_pairs(counts, rows, cfg.page, cfg.group)
+    total_pairs = lb.pairs()
+    return {"value": N * (sample_pairs / total_pairs) / dt, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle: top-K selection of the last chunk's query pages, then "
+                      f"fwd+bwd of the last {rows} query rows x {cfg.hq} heads on it "
+                      f"({sample_pairs} attended pairs x heads of {total_pairs}); {dt:.1f}s, "
+                      "scaled by the pair share"}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -534,6 +590,18 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
     return out
 
 
+def roofline_of(ktab: dict, workload: str) -> dict:
+    """MFMA roofline of the kernel with the largest time per step: its
+    executed FLOP (per attended pair, x pairs) over its summed launch times."""
+    dom = max((k for k in ktab if k in KERNEL_FLOPS_PER_PAIR), key=lambda k: ktab[k]["ms_per_step"])
+    achieved = ktab[dom]["tflops_executed"]
+    return {"bound": "mfma", "kernel": f"{dom}_bf16_kernel", "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(dom, workload),
+            "flops_per_pair": f"{KERNEL_FLOPS_PER_PAIR[dom]}*d*Hq"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -622,13 +690,7 @@ def main():
     ktab = kernel_table(lb, ms, kt, args.steps)
     log(f"[bench] {cfg.name}: {ms:.1f} ms/step, {flops / ms / 1e9:.1f} TFLOP/s; kernels {ktab}")
 
-    dom = max((k for k in ktab if k in KERNEL_FLOPS_PER_PAIR), key=lambda k: ktab[k]["ms_per_step"])
-    achieved = ktab[dom]["tflops"]
-    roofline = {"bound": "mfma", "kernel": f"{dom}_bf16_kernel", "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_for(dom, cfg.name),
-                "flops_per_pair": f"{KERNEL_FLOPS_PER_PAIR[dom]}*d*Hq"}
+    roofline = roofline_of(ktab, cfg.name)
 
     line = {
         "metric": "attn fwd+bwd tokens/s per layer, 128K dense & 256K top-K; % bf16 MFMA peak",
@@ -654,11 +716,15 @@ def main():
                     for k, e in ktab.items()},
         "kernel_timing": "HIP events on the launching stream over a second pass of the same steps "
                          "(dQ and dK/dV then run one after the other)",
+        "flop_accounting": "tflops and mfma_frac: 14*d*Hq per attended pair (algorithmic); per "
+                           "kernel: tflops_executed (fwd 4, dq 6, dkdv 8 x d*Hq: the dQ kernel "
+                           "recomputes S and dP) and tflops_algorithmic (fwd 4, dq 2, dkdv 8)",
         "roofline": roofline,
     }
 
-    line["phases"] = phase_rates(lb)
-    log(f"[bench] phases: {line['phases']}")
+    if not cfg.sparse:
+        line["phases"] = phase_rates(lb)
+        log(f"[bench] phases: {line['phases']}")
     gemm = gemm_peak_tflops()
     line["gemm_bf16_tflops"] = round(gemm, 1)
     line["mfma_frac_of_gemm"] = round(flops / ms / 1e9 / gemm, 4)
@@ -685,7 +751,14 @@ def main():
             "attended_pairs_x_heads": spairs,
             "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                             for kk, vv in e.items()} for k, e in sktab.items()},
+            "roofline": roofline_of(sktab, scfg.name),
         }
+        if args.cpu_rows:
+            rows = max(scfg.page, (args.cpu_rows // 3) // scfg.page * scfg.page)
+            log(f"[bench] cpu baseline: oracle on {rows} rows of {scfg.name}")
+            line["topk_256k"]["cpu_baseline"] = cpu_baseline_topk(sb, rows)
+        del sb
+        torch.cuda.empty_cache()
         lb = LayerBench(cfg) if args.cpu_rows else None
 
     if args.cpu_rows:

@@ -168,13 +168,17 @@ typedef struct {
 pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
 
 /* Destroy a pool: synchronises the device, then frees everything.  NULL is
- * accepted and ignored. */
+ * accepted and ignored.  (Support call: the pages allocate the paged cache
+ * once per training run, de 2.B; this releases it.) */
 pkv_status pkv_pool_destroy(pkv_pool* pool);
 
 /* Set the page table of (layer, kv_head) from host memory: host_slots[j] is
  * the slot of logical page j, for j < n (n <= max_logical_pages; the rest of
  * the table is left as is).  Entries must be distinct and in [0, n_slots).
- * Must be called before any append to that layer.  Synchronous. */
+ * Must be called before any append to that layer.  Synchronous.  (The
+ * logical-to-physical page mapping of the paged cache, de 2.B "Paged Memory
+ * Management"; results do not depend on it, which tests use with permuted
+ * tables.) */
 pkv_status pkv_page_table_set(pkv_pool* pool, int32_t layer, int32_t kv_head,
                               const int32_t* host_slots, int32_t n);
 
@@ -312,7 +316,8 @@ pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, in
 /* Host-tier pools only: write the dK/dV pages of `layer` that the last
  * prefetch with grads brought in back to host memory (fp32 -> host gradient
  * dtype) on copy_stream, after the attention calls on `layer` issued so far
- * have finished.  `done`, if not NULL, is recorded when the copies finish.
+ * have finished (de 2.C and nl "Methodologie": the KV gradients are
+ * offloaded to CPU memory asynchronously, like the cache itself).  `done`, if not NULL, is recorded when the copies finish.
  * With host_grad_accumulate the copies go to the window's pinned staging,
  * `done` means they are staged, and the library's host threads then add
  * them into the host tier; the call first waits (on the host) until the adds
@@ -324,16 +329,20 @@ pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_s
 
 /* Host-tier pools: total bytes moved so far by pkv_prefetch_pages (host ->
  * HBM, K/V and gradients) and by pkv_writeback_grads (HBM -> host), counted
- * on the device by the copy kernels.  Synchronises the device and waits
+ * on the device by the copy kernels (measurement support: de 2.D, sparsity
+ * shrinks the offload traffic; these are the bytes that show it).  Synchronises the device and waits
  * for pending host gradient adds.  Both are 0 without a host tier. */
 pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written);
 
 /* Zero the dK/dV pool of `layer` (all slots; the host tier too in host-tier
- * mode, synchronously, after any pending host adds). */
+ * mode, synchronously, after any pending host adds).  (Support call: the
+ * gradient pool accumulates in place over the chunks of a training step, de
+ * 2.B; a new step starts it from zero.) */
 pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);
 
 /* Export (copy, never alias) pool contents of `layer` in logical order, for
- * tests and tooling:
+ * tests and tooling (support call: it undoes the paging of de 2.B so results
+ * can be compared in token order):
  *   PKV_K, PKV_V   -> dst device [n_tok][Hkv][d] kv_dtype;
  *   PKV_DK, PKV_DV -> dst device [n_tok][Hkv][d] fp32;
  *   PKV_REPS       -> dst device [n_pages][Hkv][d] fp32;

@@ -34,6 +34,12 @@ class Config:
     do_scale: float = 1.0
     planted_frac: float = 0.0
     planted_norm: float = 0.0
+    # structured queries (optional): each query page is drawn toward
+    # `query_targets` planted key pages among its candidates, its queries
+    # getting query_affinity x the sum of those pages' offsets (per KV group),
+    # so that attention concentrates on a few pages per query page
+    query_targets: int = 0
+    query_affinity: float = 0.0
     host_tier: bool = False
     hbm_cap_bytes: int = 0
     cid: int = 0          # stream id used to key the seeded substreams

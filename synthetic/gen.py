@@ -14,6 +14,13 @@ Value laws per workload:
   * planted_frac > 0: round(planted_frac * n_pages) pages per KV head, drawn
     without replacement, get one offset vector u = planted_norm * z / |z|,
     z ~ N(0, I_d), added to every key of that page-head.
+  * query_targets > 0 (structured queries): for every query page i and KV
+    head g, query_targets planted pages are drawn without replacement from
+    the planted pages of head g in [n_sink, i - n_local] (fewer if fewer
+    exist), and every query of page i in a head of group g gets
+    query_affinity x the sum of their offsets u.  Its scores against those
+    pages' keys then rise by about query_affinity x |u|^2 each, so attention
+    concentrates on a few earlier pages per query page.
   * page table: per KV head, the first n_pages entries of a seeded
     permutation of the slot indices.
 """
@@ -26,7 +33,7 @@ import numpy as np
 
 from .configs import Config
 
-_Q, _K, _V, _DO, _TABLE, _PLANT = 1, 2, 3, 4, 5, 6
+_Q, _K, _V, _DO, _TABLE, _PLANT, _TARGET = 1, 2, 3, 4, 5, 6, 7
 _BLOCK = 512
 _POOL = None
 
@@ -162,6 +169,20 @@ class Workload:
                     if lo < hi:
                         k[lo - pos0:hi - pos0, g, :] += off
             k = k.astype(np.float32)
+        if cfg.query_targets > 0:
+            q = q.astype(np.float64)
+            G = cfg.hq // cfg.hkv
+            for i in range(pos0 // cfg.page, (pos0 + n - 1) // cfg.page + 1):
+                lo, hi = max(i * cfg.page, pos0) - pos0, min((i + 1) * cfg.page, pos0 + n) - pos0
+                for g, (pages, u) in self.planted().items():
+                    ok = np.nonzero((pages >= cfg.n_sink) & (pages <= i - cfg.n_local))[0]
+                    if ok.size == 0:
+                        continue
+                    r = np.random.default_rng(np.random.SeedSequence(
+                        [self.seed, cfg.cid, self.layer, i, _TARGET, g]))
+                    pick = r.choice(ok, size=min(cfg.query_targets, ok.size), replace=False)
+                    q[lo:hi, g * G:(g + 1) * G, :] += cfg.query_affinity * u[pick].sum(axis=0)
+            q = q.astype(np.float32)
         if cfg.rope_base:
             q = _rope(q, pos0, cfg.rope_base)
             k = _rope(k, pos0, cfg.rope_base)
