@@ -307,9 +307,14 @@ pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
  * only pages causal attention of that chunk reads or whose gradients it
  * changes (de 2.C: prefetch of the next layer's KV; the chunk attends to
  * every earlier page plus its own, de 2.A).  pkv_writeback_grads then writes
- * back the same pages.  1 <= n_keys <= the layer's appended length, else
+ * back the same pages.  1 <= n_keys <= max_logical_pages x P, else
  * PKV_EINVAL; ceil(n_keys / P) pages must fit window_slots, else
- * PKV_ECAPACITY. */
+ * PKV_ECAPACITY.  n_keys may reach past the keys appended so far: the window
+ * then holds the pages of the keys to come, and a later pkv_append_kv of
+ * rows below n_keys writes them into the window as well as the host tier
+ * (on its stream, after the fetch), so the next layer of a forward sweep can
+ * be prefetched before its chunk is appended (de 2.C: the next layer is
+ * fetched while the current one computes). */
 pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t with_grads,
                                hipStream_t copy_stream, hipEvent_t ready);
 
@@ -357,15 +362,24 @@ pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst
  * kv_dtype; PKV_DK, PKV_DV -> dst device [n_tok][Hkv][d] fp32.  A
  * chunk-recurrent backward reads its own chunk's completed dK/dV this way to
  * carry them back through the K/V projections (sciencestack Figure 3: the
- * pool's gradients leave the attention outside the autograd graph).  Pools
- * without a host tier (else PKV_EUNSUPPORTED); the rows must have been
- * appended (else PKV_EINVAL). */
+ * pool's gradients leave the attention outside the autograd graph).  The
+ * rows must have been appended (else PKV_EINVAL).  Host-tier pools: read
+ * from the HBM window holding the layer, on `stream` after the window's
+ * fetch, so the rows must lie below the keys its last prefetch covered
+ * (else PKV_ESTATE, also when the layer is not in its window, or for dK/dV
+ * when the window holds no gradients of the layer) and their pages must be
+ * among those it fetched: a chunk's own pages are, for any selection of
+ * pkv_select_topk_pages (its query page is always kept) and for a prefix
+ * prefetch up to the chunk's end.  The dK/dV read there are the window's:
+ * the accumulated sums when the prefetch fetched them, or only this visit's
+ * contributions with host_grad_accumulate. */
 pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t pos0,
                          int64_t n_tok, void* dst, hipStream_t stream);
 
 /* Forget the tokens of `layer` (length back to 0) so that a new sequence can
  * be appended; no memory is freed or cleared (gradients are left as they
- * are: pkv_grad_zero clears them).  Host-only, immediate. */
+ * are: pkv_grad_zero clears them; a host-tier window holding the layer then
+ * covers no keys until the next prefetch).  Host-only, immediate. */
 pkv_status pkv_pool_reset(pkv_pool* pool, int32_t layer);
 
 /* Kernel timing.  While enabled, every kernel the library launches is

@@ -317,19 +317,22 @@ int64_t pages_of(const pkv_pool* p, int layer) {
 
 }  // namespace
 
-hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStream_t s) {
+hipError_t launch_window_list(const pkv_pool* p, int layer, int window, int64_t n_pages,
+                              hipStream_t s) {
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
   const int32_t* table = p->d_table + (int64_t)layer * need_words(p);
+  // pages the map can mark: the appended ones, or those a prefix reserves
+  int64_t np = pages_of(p, layer) > n_pages ? pages_of(p, layer) : n_pages;
+  if (np > d.max_logical_pages) np = d.max_logical_pages;
   hipLaunchKernelGGL(need_compact_kernel, dim3(1), dim3(1024), 0, s, L.need, table,
-                     d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)pages_of(p, layer),
+                     d.max_logical_pages, d.n_slots, d.n_kv_heads, (int)np,
                      p->window_slots, L.items, L.count, p->d_wtable + window * need_words(p));
   return hipGetLastError();
 }
 
 hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
                         bool with_grads) {
-  if (pages_of(p, layer) <= 0) return hipSuccess;
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
   const int grad_mode = with_grads ? (d.host_grad_dtype == PKV_BF16 ? 1 : 2) : 0;
@@ -346,7 +349,6 @@ hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
 }
 
 hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hipStream_t s) {
-  if (pages_of(p, layer) <= 0) return hipSuccess;
   const pkv_pool_desc& d = p->desc;
   const WindowList L = window_list(p, window);
   hipLaunchKernelGGL(window_grad_zero_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count,

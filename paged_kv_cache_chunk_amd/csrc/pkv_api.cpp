@@ -202,6 +202,10 @@ pkv_status pkv_pool_reset(pkv_pool* pool, int32_t layer) {
   if (layer < 0 || layer >= pool->desc.n_layers)
     return fail(PKV_EINVAL, "pkv_pool_reset: layer %d out of range", layer);
   pool->length[layer] = 0;
+  // a window holding the layer no longer covers any of its keys: attention
+  // and appends need a new prefetch
+  const int w = pool->window_of(layer);
+  if (pool->desc.host_tier && pool->window_layer[w] == layer) pool->window_keys[w] = 0;
   return PKV_OK;
 }
 
@@ -480,11 +484,24 @@ pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t po
   if (layer < 0 || layer >= pool->desc.n_layers)
     return fail(PKV_EINVAL, "pkv_read_rows: layer %d out of range", layer);
   if (what < PKV_K || what > PKV_DV) return fail(PKV_EINVAL, "pkv_read_rows: bad `what` %d", what);
-  if (pool->desc.host_tier)
-    return fail(PKV_EUNSUPPORTED, "pkv_read_rows: pools without a host tier only");
   if (pos0 < 0 || n_tok < 0 || pos0 + n_tok > pool->length[layer])
     return fail(PKV_EINVAL, "pkv_read_rows: rows [%lld, %lld) outside the %lld appended",
                 (long long)pos0, (long long)(pos0 + n_tok), (long long)pool->length[layer]);
+  if (n_tok == 0) return PKV_OK;
+  if (pool->desc.host_tier) {
+    // from the HBM window that holds the layer (after its fetch; the next
+    // prefetch into the window waits for this read)
+    const int w = pool->window_of(layer);
+    if ((what == PKV_DK || what == PKV_DV) && pool->window_layer[w] == layer &&
+        !pool->window_grads[w])
+      return fail(PKV_ESTATE, "pkv_read_rows: the window holds no gradients of layer %d", layer);
+    pkv_status st = pool_before_compute(pool, layer, pos0 + n_tok, stream, false);
+    if (st != PKV_OK) return st;
+    hipError_t e = launch_export(layer_view(pool, layer), compute_geom(pool), what, pool->kv_bytes,
+                                 n_tok, dst, stream, pos0);
+    if (e != hipSuccess) return hip_fail(e, "pkv_read_rows: launch");
+    return pool_after_compute(pool, layer, stream);
+  }
   hipError_t e = launch_export(layer_view(pool, layer), geom(pool), what, pool->kv_bytes, n_tok,
                                dst, stream, pos0);
   if (e != hipSuccess) return hip_fail(e, "pkv_read_rows: launch");
@@ -510,9 +527,10 @@ pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, in
   if (!pool) return fail(PKV_EINVAL, "pkv_prefetch_prefix: null pool");
   if (layer < 0 || layer >= pool->desc.n_layers)
     return fail(PKV_EINVAL, "pkv_prefetch_prefix: layer %d out of range", layer);
-  if (n_keys < 1 || n_keys > pool->length[layer])
-    return fail(PKV_EINVAL, "pkv_prefetch_prefix: n_keys=%lld outside [1, %lld appended]",
-                (long long)n_keys, (long long)pool->length[layer]);
+  const int64_t cap = (int64_t)pool->desc.max_logical_pages * pool->desc.page_size;
+  if (n_keys < 1 || n_keys > cap)
+    return fail(PKV_EINVAL, "pkv_prefetch_prefix: n_keys=%lld outside [1, %lld]",
+                (long long)n_keys, (long long)cap);
   if (!pool->desc.host_tier) {
     if (ready) PKV_HIP(hipEventRecord(ready, copy_stream), "pkv_prefetch_prefix: hipEventRecord");
     return PKV_OK;

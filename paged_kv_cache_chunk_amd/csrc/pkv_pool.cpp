@@ -213,6 +213,14 @@ pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, cons
   const int64_t last = (pos0 + n_tok - 1) / g.page;
   e = launch_reps(L, g, p->desc.kv_dtype == PKV_BF16, first, last - first + 1, pos0 + n_tok, s);
   if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: representative launch");
+  // A prefix prefetch that reserved the window's pages for these rows: write
+  // them into the window as well (after its fetch, waited for above), so the
+  // chunk can attend to its own keys without another prefetch.
+  if (p->desc.host_tier && p->window_layer[w] == layer && pos0 + n_tok <= p->window_keys[w]) {
+    e = launch_append(layer_view(p, layer), compute_geom(p), p->kv_bytes, pos0, n_tok, k, v, s);
+    if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: window append launch");
+    return pool_after_compute(p, layer, s);  // the next prefetch into the window waits for it
+  }
   return PKV_OK;
 }
 
@@ -311,8 +319,10 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   const int w = p->window_of(layer);
   const pkv_pool_desc& d = p->desc;
   hipError_t e;
-  // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every appended key)
-  const int64_t n_avail = n_keys > 0 && n_keys < p->length[layer] ? n_keys : p->length[layer];
+  // without a selection: the pages of keys 0 .. n_keys - 1 (n_keys = 0: every
+  // appended key); n_keys may reach past the appended keys, whose pages the
+  // window then holds for appends to come
+  const int64_t n_avail = n_keys > 0 ? n_keys : p->length[layer];
   const int64_t n_pages = (n_avail + d.page_size - 1) / d.page_size;
   // the page-heads one KV head can need must fit the window's slots
   int64_t bound = n_pages;
@@ -340,7 +350,7 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   uint8_t* need = p->d_need + (int64_t)(w * 2 + b) * nw;
   if ((e = launch_need_clear(need, nw, cs)) != hipSuccess ||
       (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess ||
-      (e = launch_window_list(p, layer, w, cs)) != hipSuccess)
+      (e = launch_window_list(p, layer, w, n_pages, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");
   p->window_layer[w] = layer;
   p->window_grads[w] = with_grads;

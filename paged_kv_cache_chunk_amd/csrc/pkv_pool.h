@@ -135,7 +135,8 @@ hipError_t launch_need_clear(uint8_t* need, int64_t n, hipStream_t s);
 hipError_t launch_need_mark(uint8_t* need, const pkv_sel* sel, int hkv, int max_logical,
                             int64_t n_pages_all, hipStream_t s);
 int64_t need_words(const pkv_pool* p);  // Hkv * max_logical
-hipError_t launch_window_list(const pkv_pool* p, int layer, int window, hipStream_t s);
+hipError_t launch_window_list(const pkv_pool* p, int layer, int window, int64_t n_pages,
+                              hipStream_t s);
 hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
                         bool with_grads);
 hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hipStream_t s);

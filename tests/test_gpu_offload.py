@@ -166,7 +166,7 @@ def test_prefetch_prefix_arguments():
                                pkv.PKV_BF16, host_tier=1)
     k = torch.zeros(256, cfg.hkv, cfg.d, dtype=torch.bfloat16, device="cuda")
     pkv.pkv_append_kv(pool, 0, 0, k, k)
-    for bad in (0, 257):
+    for bad in (0, cfg.n_pages * cfg.page + 1):
         with pytest.raises(pkv.PkvError) as e:
             pkv.pkv_prefetch_prefix(pool, 0, bad)
         assert e.value.status == 1  # PKV_EINVAL
@@ -503,3 +503,44 @@ def test_many_visit_gradient_accumulation():
         g_hbm = runs["all-HBM"][1][l]
         g_f32 = runs["fp32 tier"][1][l]
         assert rel_err(g_f32[0], g_hbm[0]) < 1e-5 and rel_err(g_f32[1], g_hbm[1]) < 1e-5
+
+
+def test_prefix_prefetch_ahead_of_the_append():
+    """A forward sweep prefetches a layer's pages before its chunk is
+    appended (prefix up to the chunk's end): the append then writes the rows
+    into the window too, and the chunk's attention over the window equals the
+    all-HBM pool's, bit for bit, and the oracle.  Rows past the prefix are not
+    in the window: attention on them is PKV_ESTATE."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    cfg = SMALL
+    f = Workload(cfg).full()
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    host = pkv.pkv_pool_create(2, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16,
+                               host_tier=1)
+    res = pkv.pkv_pool_create(1, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16)
+    outs = {}
+    for name, pool in (("host", host), ("hbm", res)):
+        pkv.pkv_append_kv(pool, 0, 0, dev(f.k[:3072]), dev(f.v[:3072]))
+        if name == "host":
+            pkv.pkv_prefetch_prefix(pool, 0, 4096)        # 1024 keys not appended yet
+        pkv.pkv_append_kv(pool, 0, 3072, dev(f.k[3072:4096]), dev(f.v[3072:4096]))
+        q = dev(f.q[3072:4096])
+        o = torch.empty_like(q)
+        lse = torch.empty(cfg.hq, 1024, device="cuda")
+        pkv.pkv_attn_fwd(pool, 0, 3072, q, o, lse, cfg.scale)
+        torch.cuda.synchronize()
+        outs[name] = (o.float().cpu().numpy(), lse.cpu().numpy())
+    assert np.array_equal(outs["host"][0], outs["hbm"][0])
+    assert np.array_equal(outs["host"][1], outs["hbm"][1])
+    O_ref, _ = oracle.attn_fwd(f.q[3072:4096], f.k, f.v, 3072, cfg.scale, cfg.page)
+    assert rel_err(outs["host"][0], O_ref) < 1e-2
+    pkv.pkv_append_kv(host, 0, 4096, dev(f.k[4096:4224]), dev(f.v[4096:4224]))
+    q = dev(f.q[4096:4224])
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_attn_fwd(host, 0, 4096, q, torch.empty_like(q),
+                         torch.empty(cfg.hq, 128, device="cuda"), cfg.scale)
+    assert e.value.status == 4, str(e.value)
+    torch.cuda.synchronize()
+    host.close()
+    res.close()
