@@ -346,6 +346,69 @@ def block_bench(n_ctx: int, chunk: int, top_k: int = 0) -> dict:
             "forward_sweep_working_set_bytes": ws_fwd, "backward_sweep_working_set_bytes": ws_bwd}
 
 
+def stack_bench(n_layers: int, n_ctx: int, chunk: int, top_k: int = 0) -> dict:
+    """Chunk-recurrent training of a stack of n_layers random-initialised
+    Qwen2.5-7B-shaped attention blocks (hidden 3584, Hq 28, Hkv 4, d 128),
+    once with every pool in HBM and once with every layer's K/V (bf16) and
+    KV gradients (fp32) in pinned host memory and two HBM windows filled one
+    layer ahead on a side stream.  Reports each sweep's time, the overhead of
+    the host tier, the copy kernels' time and the share of it hidden behind
+    compute (copy time minus the added wall time, over copy time), and the
+    HBM and pinned bytes of the pools."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    from paged_kv_cache_chunk_amd.recurrent import AttentionStack
+
+    out = {"layers": n_layers, "context": n_ctx, "chunk": chunk, "top_k": top_k or None}
+    for mode in ("resident", "host_tier"):
+        torch.cuda.empty_cache()
+        st = AttentionStack(n_layers, max_tokens=n_ctx, sparse=Sparse(top_k) if top_k else None,
+                            seed=0, host_tier=mode == "host_tier")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(11)
+        xs, gys = [], []
+        for p0 in range(0, n_ctx, chunk):
+            n = min(chunk, n_ctx - p0)
+            xs.append(torch.randn(n, 3584, generator=g, device="cuda").to(torch.bfloat16))
+            gys.append((torch.randn(n, 3584, generator=g, device="cuda") / 64).to(torch.bfloat16))
+        st.forward_sweep(xs)  # warm-up step
+        st.backward_sweep(xs, gys)
+        for w in st.parameters():
+            w.grad = None
+        torch.cuda.synchronize()
+        pkv.pkv_kernel_timing(True)
+        torch.cuda.reset_peak_memory_stats()
+        t0 = time.perf_counter()
+        st.forward_sweep(xs)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st.backward_sweep(xs, gys)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        kt = pkv.pkv_kernel_times()
+        pkv.pkv_kernel_timing(False)
+        dev_b, host_b = st.pool_bytes()
+        peak = torch.cuda.max_memory_allocated()
+        out[mode] = {"forward_sweep_s": round(t1 - t0, 3), "backward_sweep_s": round(t2 - t1, 3),
+                     "tokens_per_s": round(n_ctx / (t2 - t0), 1),
+                     "fetch_ms": round(kt["fetch"][0], 1), "writeback_ms": round(kt["writeback"][0], 1),
+                     "attention_kernels_ms": round(sum(kt[k][0] for k in ("select", "fwd", "delta",
+                                                                           "dq", "dkdv")), 1),
+                     "pool_hbm_bytes": dev_b, "pool_host_bytes": host_b,
+                     "torch_peak_hbm_bytes": peak}
+        log(f"[bench] stack {mode}: {out[mode]}")
+        st.close()
+        del st, xs, gys
+    r, o = out["resident"], out["host_tier"]
+    wall_r = r["forward_sweep_s"] + r["backward_sweep_s"]
+    wall_o = o["forward_sweep_s"] + o["backward_sweep_s"]
+    copy_s = (o["fetch_ms"] + o["writeback_ms"]) / 1e3
+    out["host_tier_overhead"] = round(wall_o / wall_r - 1, 4)
+    out["copy_hidden_share"] = round(max(0.0, (copy_s - (wall_o - wall_r)) / max(copy_s, 1e-9)), 4)
+    return out
+
+
 def gemm_peak_tflops(n: int = 8192, reps: int = 20) -> float:
     """bf16 GEMM rate of the box's BLAS (torch.matmul of two contiguous
     n x n bf16 matrices, fp32 accumulate): a measured ceiling for dense bf16
@@ -629,6 +692,12 @@ def main():
                          "block at TOKENS and TOKENS/2 context (chunks of 12288; --block-top-k K "
                          "for top-K attention)")
     ap.add_argument("--block-top-k", type=int, default=0)
+    ap.add_argument("--stack", type=int, default=0, metavar="LAYERS",
+                    help="only run chunk-recurrent training of a stack of LAYERS Qwen2.5-7B-shaped "
+                         "attention blocks, all pools in HBM vs in the host tier (--stack-ctx, "
+                         "--stack-chunk, --block-top-k)")
+    ap.add_argument("--stack-ctx", type=int, default=131072)
+    ap.add_argument("--stack-chunk", type=int, default=12288)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -657,6 +726,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.stack:
+        r = stack_bench(args.stack, args.stack_ctx, args.stack_chunk, args.block_top_k)
+        print(json.dumps({"metric": "chunk-recurrent attention-stack training: host tier vs HBM",
+                          "n_gpus": 1, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
+        return
     if args.block:
         runs = [block_bench(n, 12288, args.block_top_k) for n in (args.block // 2, args.block)]
         for r in runs:
