@@ -513,7 +513,8 @@ def traffic_for(kernel: str, workload: str):
     return e.get("bytes_per_launch")
 
 
-def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) -> dict:
+def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0,
+                  select_ahead: bool = False) -> dict:
     """Host-offloaded stack: every layer's K/V and KV-gradient pools in pinned
     host memory (bf16), an HBM window of two layers, the next layer's
     selected pages prefetched on a side stream during the current layer, and
@@ -522,7 +523,10 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
     + backward + writeback); the forward sweep that appends every chunk's
     K/V to the host tier is untimed setup.  host_accumulate: the window's
     gradients start at zero and the library's host threads add each visit's
-    contributions into the host tier (no gradient bytes host -> HBM)."""
+    contributions into the host tier (no gradient bytes host -> HBM).
+    select_ahead: the selections are made before the timed backward sweep
+    (as the forward sweep makes them) and reused by it; their time is
+    reported apart."""
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -565,6 +569,16 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
 
         chunk_ids = list(reversed(range(cfg.n_chunks)))[:steps] if steps > 0 else \
             list(reversed(range(cfg.n_chunks)))
+        select_s = None
+        if sp is not None and select_ahead:
+            # the forward sweep's selections, reused by the backward sweep
+            torch.cuda.synchronize()
+            t_sel = time.perf_counter()
+            sweep.select_all(range(L), chunk_ids, inputs)
+            torch.cuda.synchronize()
+            select_s = time.perf_counter() - t_sel
+            log(f"[bench] {cfg.name} {mode}: selections of {len(chunk_ids)} chunks x {L} layers "
+                f"made ahead in {select_s:.2f}s")
         pkv.pkv_kernel_timing(True)
         torch.cuda.synchronize()
         windows = []  # (first chunk id of the window, chunks done, bytes fetched, written) so far
@@ -606,6 +620,7 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
                                "written_gb_per_layer_chunk": round((wb - prev[2]) / 1e9 / (n * L), 3)})
             prev = (done, fb, wb)
         results[mode] = {"wall_s": wall, "compute_kernels_s": compute, "copy_kernels_s": copy,
+                         "select_ahead_s": select_s,
                          "per_window": per_window,
                          "fetched_bytes": fetched, "written_bytes": written,
                          "chunks": len(chunk_ids), "hbm_bytes": dev_b, "host_bytes": host_b,
@@ -624,6 +639,8 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0) 
                     + (", gradient contributions added on the host" if host_accumulate else
                        ", gradients accumulated in HBM"),
         "host_grad_accumulate": host_accumulate,
+        "selections_made_ahead_s": (round(off["select_ahead_s"], 3)
+                                    if off["select_ahead_s"] is not None else None),
         "chunks_timed": off["chunks"],
         "tokens_per_s_per_layer": round(tokens * L / off["wall_s"], 1),
         "backward_sweep_s": round(off["wall_s"], 3),
@@ -682,6 +699,9 @@ def main():
     ap.add_argument("--host-accumulate", type=int, default=0, choices=(0, 1),
                     help="offloaded workload: add gradient contributions on the host instead of "
                          "fetching the gradients into HBM")
+    ap.add_argument("--select-ahead", action="store_true",
+                    help="offloaded top-K workload: make every selection before the timed backward "
+                         "sweep (as the forward sweep does) and reuse them")
     ap.add_argument("--resident-ab", action="store_true",
                     help="offloaded workload: also run the same sweep with all pools in HBM")
     ap.add_argument("--topk-sweep", default="", metavar="K1,K2,..",
@@ -750,7 +770,8 @@ def main():
     if cfg.host_tier:
         if args.layers:
             cfg = cfg.replace(n_layers=args.layers)
-        res = offload_bench(cfg, args.chunks, args.resident_ab, args.host_accumulate)
+        res = offload_bench(cfg, args.chunks, args.resident_ab, args.host_accumulate,
+                            args.select_ahead)
         res.update({"metric": f"offloaded {'top-K' if cfg.sparse else 'dense'} stack: "
                               "backward-sweep tokens/s per layer",
                     "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic"})

@@ -40,11 +40,12 @@ class ChunkBuffers:
         self.o = torch.empty(n_q, hq, d, dtype=dtype, device=device)
         self.lse = torch.empty(hq, n_q, dtype=torch.float32, device=device)
         self.dq = torch.empty(n_q, hq, d, dtype=torch.float32, device=device)
-        self.sel = None
+        self.sel = self.own_sel = None  # sel: the selection in use (own_sel or one kept elsewhere)
         if sparse is not None:
             nqp = -(-n_q // page)
-            self.sel = (torch.empty(nqp, hkv, sparse.stride, dtype=torch.int32, device=device),
-                        torch.empty(nqp, hkv, dtype=torch.int32, device=device))
+            self.own_sel = (torch.empty(nqp, hkv, sparse.stride, dtype=torch.int32, device=device),
+                            torch.empty(nqp, hkv, dtype=torch.int32, device=device))
+            self.sel = self.own_sel
 
 
 def chunk_step(pool: Pool, layer: int, q_pos0: int, q, do, o, lse, dq, scale: float,
@@ -76,11 +77,16 @@ class OffloadSweep:
     host adds of its window's previous writeback have freed the staging.
 
     inputs(layer, chunk) -> dict(q_pos0, q, do) of device tensors.
+
+    sels: optional {(layer, chunk): (pages, count)} made beforehand, e.g. by
+    the forward sweep (select_all): the backward sweep then reuses them (the
+    selection is a constant of the gradient) instead of selecting again
+    beside the copy kernels, whose host reads slow small kernels down.
     """
 
     def __init__(self, pool: Pool, n_layers: int, hq: int, hkv: int, d: int, page: int,
                  scale: float, sparse: Optional[Sparse], dtype: torch.dtype,
-                 compute_stream=None, copy_stream=None, writeback_stream=None):
+                 compute_stream=None, copy_stream=None, writeback_stream=None, sels=None):
         self.pool, self.L, self.hq, self.hkv, self.d, self.page = pool, n_layers, hq, hkv, d, page
         self.scale, self.sparse, self.dtype = scale, sparse, dtype
         self.compute = compute_stream or torch.cuda.current_stream()
@@ -88,12 +94,36 @@ class OffloadSweep:
         # that both directions of the host link are busy at once
         self.copy = copy_stream or torch.cuda.Stream()
         self.wb = writeback_stream or torch.cuda.Stream()
-        self.sel = {}
+        self.sels = sels
+
+    def select_all(self, layers, chunks, inputs) -> dict:
+        """Selections of the given (layer, chunk) pairs, on the compute stream
+        (what a forward sweep computes and the backward sweep reuses); kept in
+        self.sels and returned."""
+        out = {} if self.sels is None else self.sels
+        if self.sparse is None:
+            return out
+        for c in chunks:
+            for layer in layers:
+                ch = inputs(layer, c)
+                nqp = -(-ch["q"].shape[0] // self.page)
+                pages = torch.empty(nqp, self.hkv, self.sparse.stride, dtype=torch.int32,
+                                    device=ch["q"].device)
+                count = torch.empty(nqp, self.hkv, dtype=torch.int32, device=ch["q"].device)
+                pkv_select_topk_pages(self.pool, layer, ch["q_pos0"], ch["q"], self.sparse.top_k,
+                                      pages, count, self.sparse.n_sink, self.sparse.n_local,
+                                      stream=self.compute)
+                out[(layer, ch["q_pos0"])] = (pages, count)
+        self.sels = out
+        return out
 
     def _select(self, layer: int, ch: dict, buf: ChunkBuffers):
         if self.sparse is None:
             return None
-        sel = buf.sel
+        if self.sels and (layer, ch["q_pos0"]) in self.sels:
+            buf.sel = self.sels[(layer, ch["q_pos0"])]
+            return buf.sel
+        sel = buf.sel = buf.own_sel
         pkv_select_topk_pages(self.pool, layer, ch["q_pos0"], ch["q"], self.sparse.top_k,
                               sel[0], sel[1], self.sparse.n_sink, self.sparse.n_local,
                               stream=self.compute)
@@ -116,6 +146,7 @@ class OffloadSweep:
         ev.record(self.compute)
         self.copy.wait_event(ev)
         self._prefetch(layer, ch, sel)
+        return sel
 
     def chunk(self, c: int, inputs, bufs, outputs=None, next_chunk=None):
         """Backward-sweep step of chunk c over every layer.  bufs[layer]:
@@ -132,25 +163,28 @@ class OffloadSweep:
         L = self.L
         ahead = getattr(self, "_ahead", None)
         self._ahead = None
+        sels = {}
         if ahead is not None and ahead[0] == c:
             ins = {L - 1: ahead[1]}
+            sels[L - 1] = ahead[2]
         else:
             ins = {L - 1: inputs(L - 1, c)}
-            self._select_and_prefetch(L - 1, ins[L - 1], bufs[L - 1])
+            sels[L - 1] = self._select_and_prefetch(L - 1, ins[L - 1], bufs[L - 1])
         for layer in range(L - 1, -1, -1):
             if layer - 1 >= 0:
                 ins[layer - 1] = inputs(layer - 1, c)
-                self._select_and_prefetch(layer - 1, ins[layer - 1], bufs[layer - 1])
+                sels[layer - 1] = self._select_and_prefetch(layer - 1, ins[layer - 1],
+                                                            bufs[layer - 1])
             elif next_chunk is not None and L % 2 == 0:
                 c_next, bufs_next = next_chunk
                 ch_next = inputs(L - 1, c_next)
-                self._select_and_prefetch(L - 1, ch_next, bufs_next[L - 1])
-                self._ahead = (c_next, ch_next)
-            ch, b = ins.pop(layer), bufs[layer]
+                sel_next = self._select_and_prefetch(L - 1, ch_next, bufs_next[L - 1])
+                self._ahead = (c_next, ch_next, sel_next)
+            ch, b, sel = ins.pop(layer), bufs[layer], sels.pop(layer)
             pkv_attn_fwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, b.lse, self.scale,
-                         sel=b.sel, stream=self.compute)
+                         sel=sel, stream=self.compute)
             pkv_attn_bwd(self.pool, layer, ch["q_pos0"], ch["q"], b.o, ch["do"], b.lse, b.dq,
-                         self.scale, sel=b.sel, stream=self.compute)
+                         self.scale, sel=sel, stream=self.compute)
             if outputs is not None:
                 outputs(layer, c, b)
             pkv_writeback_grads(self.pool, layer, copy_stream=self.wb)

@@ -30,7 +30,7 @@ CFG = mini_config("qwen_1m_offload", n_ctx=4096, chunk=1024, n_layers=3, top_k=6
 
 
 def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0, lookahead=False,
-           window_slots=0):
+           window_slots=0, select_ahead=False):
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -71,6 +71,8 @@ def _sweep(cfg, host_tier, host_grad_dtype=None, sparse=True, accumulate=0, look
                                 torch.bfloat16, sp) for l in range(L)}
 
     order = list(reversed(range(cfg.n_chunks)))
+    if select_ahead and sp is not None:
+        sweep.select_all(range(L), order, inputs)
     nxt = bufs_for(order[0])
     for i, c in enumerate(order):
         bufs, nxt = nxt, (bufs_for(order[i + 1]) if i + 1 < len(order) else None)
@@ -544,3 +546,21 @@ def test_prefix_prefetch_ahead_of_the_append():
     torch.cuda.synchronize()
     host.close()
     res.close()
+
+
+def test_selections_made_ahead_give_the_same_sweep():
+    """The backward sweep reusing selections made before it (as a forward
+    sweep makes them) gives the results of selecting layer by layer inside
+    it: O, LSE, dQ and the selections bit for bit, dK/dV to atomic order."""
+    import paged_kv_cache_chunk_amd as pkv
+    cfg = CFG.replace(n_layers=2)
+    # fp32 host gradients: the two runs differ only in the order of fp32 adds
+    a, ga, _, _ = _sweep(cfg, True, pkv.PKV_F32, lookahead=True, select_ahead=True)
+    b, gb, _, _ = _sweep(cfg, True, pkv.PKV_F32, lookahead=True)
+    for key in b:
+        for name in ("O", "lse", "dq"):
+            assert np.array_equal(a[key][name].numpy(), b[key][name].numpy()), (key, name)
+        for x, y in zip(a[key]["sel"], b[key]["sel"]):
+            assert np.array_equal(x.numpy(), y.numpy())
+    for l in range(cfg.n_layers):
+        assert rel_err(ga[l][0], gb[l][0]) < 1e-5 and rel_err(ga[l][1], gb[l][1]) < 1e-5
