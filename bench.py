@@ -682,6 +682,111 @@ def roofline_of(ktab: dict, workload: str) -> dict:
             "flops_per_pair": f"{KERNEL_FLOPS_PER_PAIR[dom]}*d*Hq"}
 
 
+def summarize_trace(trace_dir: str) -> dict:
+    """Per-kernel totals and copy/compute overlap of a rocprofv3 kernel trace
+    (--kernel-trace --output-format csv): for each host-link copy kernel
+    (fetch_kernel, writeback_kernel), the share of its duration during which
+    at least one other kernel runs, from the trace's start/end timestamps."""
+    import bisect
+    import collections
+    import csv
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    if not rows:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    copy_names = ("fetch_kernel", "writeback_kernel")
+
+    def copy_kind(n):
+        return next((c for c in copy_names if c in n), None)
+
+    def merge(iv):
+        out = []
+        for a, b in sorted(iv):
+            if out and a <= out[-1][1]:
+                out[-1][1] = max(out[-1][1], b)
+            else:
+                out.append([a, b])
+        return out
+    comp = merge((a, b) for n, a, b in rows if copy_kind(n) is None)
+    starts = [m[0] for m in comp]
+
+    def covered(a, b):
+        tot, i = 0, max(0, bisect.bisect_right(starts, a) - 1)
+        while i < len(comp) and comp[i][0] < b:
+            x, y = max(a, comp[i][0]), min(b, comp[i][1])
+            tot += max(0, y - x)
+            i += 1
+        return tot
+    kern = collections.defaultdict(lambda: [0, 0])
+    for n, a, b in rows:
+        short = n.replace("void ", "").replace("pkv::(anonymous namespace)::", "")
+        short = short[:60] if short.startswith("at::") else short.split("(")[0]
+        kern[short][0] += 1
+        kern[short][1] += b - a
+    out = {"span_s": (max(b for _, _, b in rows) - min(a for _, a, _ in rows)) / 1e9,
+           "compute_busy_s": sum(b - a for a, b in comp) / 1e9, "copy": {}, "kernels": {}}
+    for c in copy_names:
+        iv = [(a, b) for n, a, b in rows if copy_kind(n) == c]
+        if not iv:
+            continue
+        tot = sum(b - a for a, b in iv)
+        cov = sum(covered(a, b) for a, b in iv)
+        out["copy"][c] = {"launches": len(iv), "summed_s": tot / 1e9,
+                          "concurrent_with_compute_s": cov / 1e9, "overlap": cov / max(tot, 1)}
+    for k, (n, t) in sorted(kern.items(), key=lambda x: -x[1][1]):
+        out["kernels"][k] = {"calls": n, "total_ms": t / 1e6, "avg_ms": t / 1e6 / n}
+    return out
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_write_dir: str,
+                       workload: str, cal_bytes: int = 1 << 30) -> dict:
+    """HBM bytes per launch of the library's kernels from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+    the same counter reads for a plain device copy of cal_bytes (bench.py
+    --copy-calibration); merged into profiles/traffic.json under
+    '<workload>:<kernel>' with the current kernel source hash."""
+    import collections
+    import csv
+
+    def read(d, counter):
+        acc = collections.defaultdict(list)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+    cf, cw = read(cal_fetch_dir, "FETCH_SIZE"), read(cal_write_dir, "WRITE_SIZE")
+    ck = next(k for k in cf if "copyBuffer" in k or "copy" in k.lower())
+    ff = cal_bytes / 1024 / (sum(cf[ck]) / len(cf[ck]))
+    wf = cal_bytes / 1024 / (sum(cw[ck]) / len(cw[ck]))
+    f, w = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    names = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkdv": "dkdv_bf16_kernel",
+             "gather": "gather_kernel", "atomics": "atomics_kernel"}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data.update({"_doc": "HBM bytes per launch = FETCH_SIZE*fetch_factor + WRITE_SIZE*write_factor "
+                         "(KiB -> bytes), averaged over every launch of the profiled run; factors "
+                         "from a 1 GiB device copy under the same counters",
+                 "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)})
+    h = source_hash()
+    for key, pat in names.items():
+        ks = [k for k in f if pat in k]
+        if not ks:
+            continue
+        fv = [x for k in ks for x in f[k]]
+        wv = [x for k in ks for x in w.get(k, [])]
+        fk, wk = sum(fv) / len(fv), (sum(wv) / len(wv) if wv else 0.0)
+        data[f"{workload}:{key}"] = {"source_hash": h, "bytes_per_launch": int(1024 * (fk * ff + wk * wf)),
+                                     "fetch_kib": int(fk), "write_kib": int(wk), "launches": len(fv)}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1)
+    return data
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -721,7 +826,23 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--summarize-trace", default="", metavar="DIR",
+                    help="only print per-kernel totals and copy/compute overlap of a rocprofv3 "
+                         "kernel trace under DIR (no GPU)")
+    ap.add_argument("--summarize-counters", nargs=5, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "WORKLOAD"),
+                    help="only merge rocprofv3 FETCH_SIZE / WRITE_SIZE runs into profiles/traffic.json "
+                         "(no GPU)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1), flush=True)
+        return
+    if args.summarize_counters:
+        d = summarize_counters(*args.summarize_counters)
+        print(json.dumps({k: v for k, v in d.items() if k.startswith(args.summarize_counters[4])},
+                         indent=1), flush=True)
+        return
 
     if args.copy_calibration:
         import torch
