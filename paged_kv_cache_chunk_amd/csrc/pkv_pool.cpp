@@ -19,9 +19,19 @@
 namespace pkv {
 namespace {
 
+// Test hook: PKV_FAIL_ALLOC_AT=n makes the n-th device or pinned allocation
+// of a pool creation fail as if memory were exhausted, so that tests can
+// check that a half-built pool is released completely.
+bool injected_failure(pkv_pool* p) {
+  const char* now = std::getenv("PKV_FAIL_ALLOC_AT");
+  if (!now) return false;
+  return ++p->allocs == std::atoi(now);
+}
+
 pkv_status dev_alloc(pkv_pool* p, void** ptr, int64_t bytes, const char* what) {
   *ptr = nullptr;
   if (bytes <= 0) return PKV_OK;
+  if (injected_failure(p)) return pool_fail(PKV_ENOMEM, "injected allocation failure (PKV_FAIL_ALLOC_AT)");
   hipError_t e = hipMalloc(ptr, (size_t)bytes);
   if (e != hipSuccess) {
     *ptr = nullptr;
@@ -36,6 +46,7 @@ pkv_status dev_alloc(pkv_pool* p, void** ptr, int64_t bytes, const char* what) {
 
 pkv_status host_alloc(pkv_pool* p, void** hptr, void** dptr, int64_t bytes) {
   *hptr = *dptr = nullptr;
+  if (injected_failure(p)) return pool_fail(PKV_ENOMEM, "injected allocation failure (PKV_FAIL_ALLOC_AT)");
   hipError_t e = hipHostMalloc(hptr, (size_t)bytes, hipHostMallocMapped);
   if (e != hipSuccess) {
     *hptr = nullptr;
@@ -144,6 +155,8 @@ pkv_status pool_allocate(pkv_pool* p) {
       for (int w = 0; w < pkv_pool::kWindow; ++w) {
         if ((st = host_alloc(p, &p->h_stage_dk[w], &p->m_stage_dk[w], hgr)) != PKV_OK) return st;
         if ((st = host_alloc(p, &p->h_stage_dv[w], &p->m_stage_dv[w], hgr)) != PKV_OK) return st;
+        if (injected_failure(p))
+          return pool_fail(PKV_ENOMEM, "injected allocation failure (PKV_FAIL_ALLOC_AT)");
         if ((e = hipHostMalloc((void**)&p->h_stage_need[w], (size_t)need_w, hipHostMallocDefault)) !=
             hipSuccess) {
           p->h_stage_need[w] = nullptr;

@@ -92,3 +92,54 @@ def test_rejected_calls_and_recovery():
     O_ref, _ = oracle.attn_fwd(f.q[ch.q_pos0:], f.k, f.v, ch.q_pos0, cfg.scale, cfg.page)
     assert rel_err(o.cpu().numpy(), O_ref) <= 1e-5
     pool.close()
+
+
+@pytest.mark.parametrize("host_tier", [0, 1])
+def test_failed_pool_creation_releases_everything(host_tier):
+    """Every allocation of a pool creation, failed in turn through the
+    library's test hook (PKV_FAIL_ALLOC_AT=n: the n-th device or pinned
+    allocation fails as if memory were exhausted), returns PKV_ENOMEM and
+    releases what the half-built pool had allocated: device free memory is
+    back at its level before the attempts, and a pool created afterwards
+    works (its forward matches the oracle)."""
+    import os
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    kw = dict(host_tier=1, host_grad_accumulate=1, window_slots=36) if host_tier else {}
+    failed = 0
+    for n in range(1, 80):
+        os.environ["PKV_FAIL_ALLOC_AT"] = str(n)
+        try:
+            pool = pkv.pkv_pool_create(2, 4, 128, 128, 64, 64, pkv.PKV_BF16, **kw)
+        except pkv.PkvError as e:
+            assert e.status == 2 and "injected" in str(e), str(e)
+            failed += 1
+            continue
+        finally:
+            del os.environ["PKV_FAIL_ALLOC_AT"]
+        pool.close()  # n past the last allocation: created normally
+        break
+    assert failed >= (20 if host_tier else 6), failed
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert abs(free1 - free0) < (64 << 20), (free0, free1)
+    cfg = get_config("tiny_f32")
+    w = Workload(cfg)
+    f = w.full()
+    pool = pkv.pkv_pool_create(1, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_F32,
+                               host_tier=host_tier)
+    dev = lambda x: torch.from_numpy(x).cuda()
+    pkv.pkv_append_kv(pool, 0, 0, dev(f.k), dev(f.v))
+    if host_tier:
+        pkv.pkv_prefetch_pages(pool, 0)
+    q = dev(f.q[128:256])
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.hq, 128, device="cuda")
+    pkv.pkv_attn_fwd(pool, 0, 128, q, o, lse, cfg.scale)
+    torch.cuda.synchronize()
+    O_ref, _ = oracle.attn_fwd(f.q[128:256], f.k, f.v, 128, cfg.scale, cfg.page)
+    assert rel_err(o.cpu().numpy(), O_ref) <= 1e-5
+    pool.close()
