@@ -1,0 +1,112 @@
+"""Property tests of the fp64 oracle over random small shapes (hypothesis):
+for any context length (ragged last chunk and last page included), page
+size, chunk size (a multiple of the page), GQA ratio, head dim, top-K budget
+and forced-page counts, the vectorised oracle agrees with the pure-loop
+brute force, processing in chunks gives the result of one chunk, the
+gradient sums of the softmax hold, a budget covering every page reproduces
+dense attention, and the selection equals a plain sort of (score, page).
+CPU only; each example is tiny."""
+import numpy as np
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from oracle.brute import attn_brute, brute_select
+
+
+@st.composite
+def shapes(draw):
+    page = draw(st.sampled_from([2, 4, 8]))
+    chunk = page * draw(st.integers(1, 3))
+    n = draw(st.integers(1, 5 * page + page - 1))
+    hkv = draw(st.integers(1, 2))
+    g = draw(st.integers(1, 3))
+    d = draw(st.sampled_from([4, 8]))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((n, hkv * g, d))
+    k = r.standard_normal((n, hkv, d))
+    v = r.standard_normal((n, hkv, d))
+    do = r.standard_normal((n, hkv * g, d))
+    scale = float(draw(st.sampled_from([0.3, 1.0 / np.sqrt(d)])))
+    return q, k, v, do, page, chunk, scale
+
+
+SETTINGS = settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+NAMES = (("O", 0), ("lse", 1), ("dq", 2), ("dk", 3), ("dv", 4))
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.abs(a - b).max() / max(np.abs(b).max(), 1e-300)
+
+
+@SETTINGS
+@given(shapes())
+def test_dense_matches_brute_force(s):
+    q, k, v, do, page, chunk, scale = s
+    r = oracle.run_chunks(q, k, v, do, chunk, scale, page)
+    b = attn_brute(q.tolist(), k.tolist(), v.tolist(), do.tolist(), chunk, scale, page)
+    for name, i in NAMES:
+        assert np.abs(np.array(b[i]) - r[name]).max() < 1e-11, name
+
+
+@SETTINGS
+@given(shapes(), st.integers(0, 4), st.integers(0, 2), st.integers(1, 3))
+def test_sparse_matches_brute_force(s, top_k, n_sink, n_local):
+    q, k, v, do, page, chunk, scale = s
+    sp = dict(top_k=top_k, n_sink=n_sink, n_local=n_local)
+    r = oracle.run_chunks(q, k, v, do, chunk, scale, page, sparse=sp)
+    sels = [[[list(map(int, x)) for x in row] for row in sel] for sel in r["sel"]]
+    b = attn_brute(q.tolist(), k.tolist(), v.tolist(), do.tolist(), chunk, scale, page, sels)
+    for name, i in NAMES:
+        assert np.abs(np.array(b[i]) - r[name]).max() < 1e-11, name
+
+
+@SETTINGS
+@given(shapes())
+def test_chunking_and_sum_identities(s):
+    q, k, v, do, page, chunk, scale = s
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    G = hq // hkv
+    a = oracle.run_chunks(q, k, v, do, chunk, scale, page)
+    one = oracle.run_chunks(q, k, v, do, n, scale, page)  # a single chunk
+    for name in ("O", "lse", "dq", "dk", "dv"):
+        assert _rel(a[name], one[name]) < 1e-12, name
+    for g in range(hkv):
+        # every row of dS sums to 0, every row of P to 1
+        assert np.abs(a["dk"][:, g].sum(0)).max() < 1e-10 * max(1.0, np.abs(a["dk"]).max())
+        want = do[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        assert _rel(a["dv"][:, g].sum(0), want) < 1e-12
+
+
+@SETTINGS
+@given(shapes(), st.integers(0, 2), st.integers(1, 3))
+def test_budget_covering_every_page_is_dense(s, n_sink, n_local):
+    q, k, v, do, page, chunk, scale = s
+    n = q.shape[0]
+    dense = oracle.run_chunks(q, k, v, do, chunk, scale, page)
+    sparse = oracle.run_chunks(q, k, v, do, chunk, scale, page,
+                               sparse=dict(top_k=-(-n // page), n_sink=n_sink, n_local=n_local))
+    for name in ("O", "lse", "dq", "dk", "dv"):
+        assert _rel(sparse[name], dense[name]) < 1e-13, name
+
+
+@SETTINGS
+@given(shapes(), st.integers(0, 5), st.integers(0, 2), st.integers(1, 3), st.booleans())
+def test_selection_is_a_sort_of_scores(s, top_k, n_sink, n_local, ties):
+    q, k, v, do, page, chunk, scale = s
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if ties:  # copies of one page: equal scores, decided by the page index
+        for j in range(2, -(-n // page)):
+            lo, hi = j * page, min((j + 1) * page, n)
+            if hi - lo == page:
+                k[lo:hi] = k[page:2 * page] if n >= 2 * page else k[lo:hi]
+    for q_pos0 in range(0, n, chunk):
+        qc = q[q_pos0:q_pos0 + chunk]
+        got = oracle.select_pages(qc, k, q_pos0, page, hkv, top_k, n_sink, n_local)
+        want = brute_select(qc.tolist(), k[:q_pos0 + qc.shape[0]].tolist(), q_pos0, page, hkv,
+                            top_k, n_sink, n_local)
+        assert [[list(map(int, x)) for x in row] for row in got] == want
