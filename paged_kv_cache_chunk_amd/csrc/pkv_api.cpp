@@ -491,11 +491,10 @@ pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t po
   if (pool->desc.host_tier) {
     // from the HBM window that holds the layer (after its fetch; the next
     // prefetch into the window waits for this read)
-    const int w = pool->window_of(layer);
-    if ((what == PKV_DK || what == PKV_DV) && pool->window_layer[w] == layer &&
-        !pool->window_grads[w])
-      return fail(PKV_ESTATE, "pkv_read_rows: the window holds no gradients of layer %d", layer);
-    pkv_status st = pool_before_compute(pool, layer, pos0 + n_tok, stream, false);
+    // gradient rows: the window must hold this visit's gradients (and their
+    // zeroing, with host adds, must have run), as for an attention backward
+    const bool grads = what == PKV_DK || what == PKV_DV;
+    pkv_status st = pool_before_compute(pool, layer, pos0 + n_tok, stream, grads);
     if (st != PKV_OK) return st;
     hipError_t e = launch_export(layer_view(pool, layer), compute_geom(pool), what, pool->kv_bytes,
                                  n_tok, dst, stream, pos0);
