@@ -75,7 +75,11 @@ def select_pages(q: np.ndarray, k_all: np.ndarray, q_pos0: int, page: int,
             cand = np.arange(n_sink, i - n_local + 1, dtype=np.int64)
             forced = set(range(0, min(n_sink, i + 1))) | set(range(max(0, i - n_local + 1), i + 1))
             if cand.size:
-                s64 = kbar[cand, g, :] @ qbar[il, g, :]
+                # sum over e of kbar_e * qbar_e, evaluated the same way for
+                # every candidate, so that pages with equal representatives
+                # score equal and the tie rule decides between them (a BLAS
+                # matrix-vector product may round equal rows differently)
+                s64 = (kbar[cand, g, :] * qbar[il, g, :][None, :]).sum(axis=1)
                 if score_dtype == np.float32:
                     kb = kbar[cand, g, :].astype(np.float32)
                     qb = qbar[il, g, :].astype(np.float32)

@@ -110,3 +110,25 @@ def test_selection_is_a_sort_of_scores(s, top_k, n_sink, n_local, ties):
         want = brute_select(qc.tolist(), k[:q_pos0 + qc.shape[0]].tolist(), q_pos0, page, hkv,
                             top_k, n_sink, n_local)
         assert [[list(map(int, x)) for x in row] for row in got] == want
+
+
+def test_equal_pages_tie_to_the_lower_pages():
+    """Pages that are copies of one page have equal representatives, so their
+    scores must be equal and the tie rule (lower page first) must pick among
+    them: with page 0 opposite to the copies and the query mean along them,
+    top-3 keeps pages 1, 2, 3.  Many draws: a scoring that rounds equal rows
+    differently (a BLAS matrix-vector product can) fails some of them."""
+    page, n_pages, top_k = 4, 14, 3
+    for seed in range(200):
+        rng = np.random.default_rng(seed)
+        d = (4, 8, 128)[seed % 3]
+        base = rng.standard_normal((page, 1, d))
+        k = np.concatenate([-base] + [base] * (n_pages - 1))
+        q = np.repeat(base.mean(axis=0)[None], page, axis=0)  # one query page, one head
+        q_pos0 = (n_pages - 1) * page
+        for dtype in (np.float64, np.float32):
+            sel = oracle.select_pages(q, k, q_pos0, page, 1, top_k, n_sink=0, n_local=1,
+                                      score_dtype=dtype)
+            assert sel[0][0].tolist() == [1, 2, 3, n_pages - 1], (seed, d, dtype)
+        assert brute_select(q.tolist(), k.tolist(), q_pos0, page, 1, top_k, 0, 1) == \
+            [[[1, 2, 3, n_pages - 1]]]
