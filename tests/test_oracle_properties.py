@@ -32,7 +32,10 @@ def shapes(draw):
     return q, k, v, do, page, chunk, scale
 
 
-SETTINGS = settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+# derandomize: every run checks the same examples, so the suite's result does
+# not depend on the run
+SETTINGS = settings(max_examples=150, deadline=None, derandomize=True,
+                    suppress_health_check=[HealthCheck.too_slow])
 NAMES = (("O", 0), ("lse", 1), ("dq", 2), ("dk", 3), ("dv", 4))
 
 
