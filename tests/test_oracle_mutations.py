@@ -1,8 +1,9 @@
 """Planted mistakes in the fp64 oracle must fail its pins.  CPU only.
 
 Each case rewrites one line of an oracle function (a dropped scale or term, a
-flipped sign, an off-by-one causal boundary, a wrong head-to-group mapping, a
-transposed operand, a reversed tie order, a misplaced forced page, ...), puts
+flipped sign, an off-by-one causal boundary or page mask, a wrong head-to-group
+mapping, a transposed or swapped operand, a reversed tie order, a misplaced or
+missing forced page, one page too many, ...), puts
 the rewritten function in place of the original for the duration of the case,
 and runs every pin of tests/test_oracle_pins.py against it; at least one pin
 must fail.  The pure-loop brute force (oracle/brute.py), the hand-worked and
@@ -62,6 +63,22 @@ MUTANTS = {
     "key_mean_skips_first_token": (OS, "key_page_means", "k[j * page:min((j + 1) * page, n)]",
                                    "k[j * page + 1:min((j + 1) * page, n)]"),
     "depage_wrong_slot": (OA, "depage", "pool[g, table[g, j], :hi - lo]", "pool[g, j, :hi - lo]"),
+    "scores_without_scale": (OA, "_rows", "S = scale * (q @ k.T)", "S = (q @ k.T)"),
+    "probabilities_unnormalised": (OA, "_rows", "P = E / Z", "P = E"),
+    "lse_in_base_2": (OA, "_rows", "lse = (m + np.log(Z))[:, 0]", "lse = (m + np.log2(Z))[:, 0]"),
+    "D_without_O": (OA, "_rows", "D = (do * O).sum(axis=1, keepdims=True)",
+                    "D = do.sum(axis=1, keepdims=True)"),
+    "dP_with_keys": (OA, "_rows", "dP = do @ v.T", "dP = do @ k.T"),
+    "dk_from_dO": (OA, "_chunk", 'dk[:nk, g] += scale * (res["dS"].T @ q[r0:r1, h])',
+                   'dk[:nk, g] += scale * (res["dS"].T @ do[r0:r1, h])'),
+    "rows_ignore_chunk_start": (OA, "_chunk", "t_abs = q_pos0 + np.arange(r0, r1)",
+                                "t_abs = np.arange(r0, r1) + 0 * q_pos0"),
+    "page_mask_shifted": (OA, "_mask", "m &= pages_ok[:, s // page]",
+                          "m &= pages_ok[:, np.minimum(s + 1, n_keys - 1) // page]"),
+    "sinks_dropped": (OS, "select_pages", "forced = set(range(0, min(n_sink, i + 1))) | ",
+                      "forced = set() | "),
+    "one_page_too_many": (OS, "select_pages", "keep = cand[order[:min(top_k, cand.size)]]",
+                          "keep = cand[order[:min(top_k + 1, cand.size)]]"),
 }
 
 
