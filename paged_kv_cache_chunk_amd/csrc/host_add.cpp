@@ -1,7 +1,7 @@
 // Host-side accumulation of staged gradient contributions into the host
 // tier: a coordinator thread takes jobs in order, waits for the staging
-// copies' event, lists the staged page-heads from the copied page map, and
-// splits them over a small team of threads.  bf16 sums are rounded to
+// copies' event, lists the staged page-heads (from the copied window list, or
+// from the copied page map), and splits them over a small team of threads.  bf16 sums are rounded to
 // nearest-even, as the device's conversion does.
 #include "host_add.h"
 
@@ -51,15 +51,15 @@ bool has_avx2() {
   return v;
 }
 
-void add(void* dst, const void* src, int64_t e0, int64_t n, bool bf16) {
+void add(void* dst, int64_t d0, const void* src, int64_t s0, int64_t n, bool bf16) {
   const bool kAvx2 = has_avx2();
   if (bf16) {
-    uint16_t* d = (uint16_t*)dst + e0;
-    const uint16_t* s = (const uint16_t*)src + e0;
+    uint16_t* d = (uint16_t*)dst + d0;
+    const uint16_t* s = (const uint16_t*)src + s0;
     kAvx2 ? add_bf16_avx2(d, s, n) : add_bf16_base(d, s, n);
   } else {
-    float* d = (float*)dst + e0;
-    const float* s = (const float*)src + e0;
+    float* d = (float*)dst + d0;
+    const float* s = (const float*)src + s0;
     kAvx2 ? add_f32_avx2(d, s, n) : add_f32_base(d, s, n);
   }
 }
@@ -114,8 +114,9 @@ void HostAdder::run_items() {
   for (;;) {
     const int64_t i = next_.fetch_add(1, std::memory_order_relaxed);
     if (i >= n) break;
-    add(cur_.dst_dk, cur_.src_dk, items_[i], cur_.page_elems, cur_.bf16);
-    add(cur_.dst_dv, cur_.src_dv, items_[i], cur_.page_elems, cur_.bf16);
+    const auto [src, dst] = items_[i];
+    add(cur_.dst_dk, dst, cur_.src_dk, src, cur_.page_elems, cur_.bf16);
+    add(cur_.dst_dv, dst, cur_.src_dv, src, cur_.page_elems, cur_.bf16);
   }
 }
 
@@ -133,13 +134,24 @@ void HostAdder::coordinator() {
     if (e == hipSuccess) {
       cur_ = std::move(job.second);
       items_.clear();
-      for (int g = 0; g < cur_.hkv; ++g)
-        for (int j = 0; j < cur_.n_pages; ++j) {
-          const int64_t at = (int64_t)g * cur_.max_logical + j;
-          const int slot = cur_.table[at];
-          if (cur_.need[at] && slot >= 0 && slot < cur_.slots)
-            items_.push_back(((int64_t)g * cur_.slots + slot) * cur_.page_elems);
+      const int64_t tier_heads = (int64_t)cur_.hkv * cur_.slots;
+      if (cur_.list) {
+        for (int i = 0; i < cur_.n_list; ++i) {
+          const int64_t h = cur_.list[i].x;
+          if (h >= 0 && h < tier_heads)
+            items_.emplace_back((int64_t)i * cur_.page_elems, h * cur_.page_elems);
         }
+      } else {
+        for (int g = 0; g < cur_.hkv; ++g)
+          for (int j = 0; j < cur_.n_pages; ++j) {
+            const int64_t at = (int64_t)g * cur_.max_logical + j;
+            const int slot = cur_.table[at];
+            if (cur_.need[at] && slot >= 0 && slot < cur_.slots) {
+              const int64_t e = ((int64_t)g * cur_.slots + slot) * cur_.page_elems;
+              items_.emplace_back(e, e);
+            }
+          }
+      }
       next_.store(0, std::memory_order_relaxed);
       {
         std::lock_guard<std::mutex> lk(mu_);

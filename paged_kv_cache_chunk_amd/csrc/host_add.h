@@ -20,14 +20,19 @@
 
 namespace pkv {
 
+// The staged page-heads come either as a list (list != nullptr: staging
+// page-head i goes to tier page-head list[i].x, the window list's entries)
+// or as a page map with the layer's table (staging indexed like the tier).
 struct AddJob {
   hipEvent_t ready = nullptr;      // recorded after the staging copies
+  const int2* list = nullptr;      // [n_list] (tier page-head, window page-head), pinned
+  int n_list = 0;
   const uint8_t* need = nullptr;   // [hkv][max_logical] staged page-heads (pinned)
   std::vector<int32_t> table;      // [hkv][max_logical] logical page -> slot, a copy
   int hkv = 0, max_logical = 0, n_pages = 0, slots = 0;
   int64_t page_elems = 0;
   bool bf16 = true;                // element type of staging and tier
-  const void* src_dk = nullptr;    // staging, indexed like the tier
+  const void* src_dk = nullptr;    // staging
   const void* src_dv = nullptr;
   void* dst_dk = nullptr;          // host tier of the layer
   void* dst_dv = nullptr;
@@ -62,7 +67,8 @@ class HostAdder {
   hipError_t err_ = hipSuccess;
   // the job being split over the team
   AddJob cur_;
-  std::vector<int64_t> items_;  // element offsets of the staged page-heads
+  // element offsets of the staged page-heads: in the staging, in the tier
+  std::vector<std::pair<int64_t, int64_t>> items_;
   std::atomic<int64_t> next_{0};
   int64_t gen_ = 0;
   int pending_ = 0;             // helpers still working on generation gen_

@@ -246,6 +246,48 @@ __global__ void __launch_bounds__(256) writeback_kernel(
     atomicAdd(moved, (unsigned long long)n * 2 * page_elems * (grad_bf16 ? 2 : 4));
 }
 
+// Host accumulation with the device staging: window fp32 dK/dV of the first
+// n listed page-heads (n = min(count, cap)) -> the staging in list order,
+// page-head i of the list to staging page-head i, in the host gradient
+// dtype (dK in the first cap page-heads, dV in the next).  HBM only, so a
+// full grid; the DMA engine then carries the staging over the host link.
+__global__ void __launch_bounds__(256) stage_grads_kernel(
+    const int2* __restrict__ items, const int* __restrict__ count, int cap, int64_t page_elems,
+    bool grad_bf16, char* __restrict__ stage, const float* __restrict__ wdk,
+    const float* __restrict__ wdv, unsigned long long* __restrict__ moved) {
+  const int n = *count < cap ? *count : cap;
+  const int64_t per = page_elems / 8;  // 8 elements per step
+  const int64_t total = (int64_t)n * per;
+  const int gb = grad_bf16 ? 2 : 4;
+  char* sdk = stage;
+  char* sdv = stage + (int64_t)cap * page_elems * gb;
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t it = u / per, off = (u - it * per) * 8;
+    const int64_t src = items[it].y * page_elems + off, dst = it * page_elems + off;
+    const float4* a = reinterpret_cast<const float4*>(wdk + src);
+    const float4* b = reinterpret_cast<const float4*>(wdv + src);
+    const float4 a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+    if (grad_bf16) {
+      *reinterpret_cast<uint4*>(sdk + dst * 2) =
+          make_uint4(to_bf16(a0.x) | (to_bf16(a0.y) << 16), to_bf16(a0.z) | (to_bf16(a0.w) << 16),
+                     to_bf16(a1.x) | (to_bf16(a1.y) << 16), to_bf16(a1.z) | (to_bf16(a1.w) << 16));
+      *reinterpret_cast<uint4*>(sdv + dst * 2) =
+          make_uint4(to_bf16(b0.x) | (to_bf16(b0.y) << 16), to_bf16(b0.z) | (to_bf16(b0.w) << 16),
+                     to_bf16(b1.x) | (to_bf16(b1.y) << 16), to_bf16(b1.z) | (to_bf16(b1.w) << 16));
+    } else {
+      float4* dk = reinterpret_cast<float4*>(sdk + dst * 4);
+      float4* dv = reinterpret_cast<float4*>(sdv + dst * 4);
+      dk[0] = a0;
+      dk[1] = a1;
+      dv[0] = b0;
+      dv[1] = b1;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && n)
+    atomicAdd(moved, (unsigned long long)n * 2 * page_elems * gb);
+}
+
 // dst[t][g][:] (fp32) = bf16 host gradient of token t
 __global__ void export_bf16_grad_kernel(const unsigned short* __restrict__ src,
                                         float* __restrict__ dst, const int32_t* __restrict__ table,
@@ -371,6 +413,28 @@ hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipS
                      (const float*)(p->d_dk + window * p->dev_elems),
                      (const float*)(p->d_dv + window * p->dev_elems), p->d_moved + 1);
   return hipGetLastError();
+}
+
+hipError_t launch_writeback_staged(const pkv_pool* p, int window, int n, hipStream_t s) {
+  const pkv_pool_desc& d = p->desc;
+  const WindowList L = window_list(p, window);
+  const int64_t page_elems = (int64_t)d.page_size * d.head_dim;
+  const int gb = d.host_grad_dtype == PKV_BF16 ? 2 : 4;
+  const int cap = (int)p->stage_heads;
+  const size_t bytes = (size_t)n * page_elems * gb;
+  KernelTimer t(KT_WRITEBACK, s);  // the conversion and the copies over the link
+  hipLaunchKernelGGL(stage_grads_kernel, dim3(2048), dim3(256), 0, s, L.items, L.count, cap,
+                     page_elems, gb == 2, p->d_stage, (const float*)(p->d_dk + window * p->dev_elems),
+                     (const float*)(p->d_dv + window * p->dev_elems), p->d_moved + 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n == 0) return e;
+  if ((e = hipMemcpyAsync(p->h_stage_dk[window], p->d_stage, bytes, hipMemcpyDeviceToHost, s)) !=
+          hipSuccess ||
+      (e = hipMemcpyAsync(p->h_stage_dv[window], p->d_stage + (size_t)cap * page_elems * gb, bytes,
+                          hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return e;
+  return hipMemcpyAsync(p->h_stage_items[window], L.items, (size_t)n * sizeof(int2),
+                        hipMemcpyDeviceToHost, s);
 }
 
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,

@@ -91,9 +91,14 @@ pkv_status pool_allocate(pkv_pool* p) {
   const int64_t needb = d.host_tier ? (int64_t)2 * pkv_pool::kWindow * d.n_kv_heads * d.max_logical_pages : 0;
   const int64_t itemb = d.host_tier ? (int64_t)8 * 2 * pkv_pool::kWindow * d.n_kv_heads * p->window_slots : 0;
   const int64_t countb = 4 * 2 * pkv_pool::kWindow;
-  if (d.host_tier && d.device_budget_bytes > 0 &&
-      2 * kvb + 2 * grb + repb + tabb + wtabb + needb + itemb + countb + 16 > d.device_budget_bytes)
+  const int64_t base_b = 2 * kvb + 2 * grb + repb + tabb + wtabb + needb + itemb + countb + 16;
+  if (d.host_tier && d.device_budget_bytes > 0 && base_b > d.device_budget_bytes)
     return pool_fail(PKV_ENOMEM, "host-tier window does not fit device_budget_bytes");
+  // host accumulation: the device staging of the writeback, where the budget
+  // leaves room for it (else the writeback kernel writes the pinned staging)
+  const int64_t stage_heads = (int64_t)d.n_kv_heads * p->window_slots;
+  const int64_t stageb = p->accumulate ? 2 * stage_heads * d.page_size * d.head_dim * grad_host_bytes(p) : 0;
+  const bool with_stage = p->accumulate && (d.device_budget_bytes <= 0 || base_b + stageb <= d.device_budget_bytes);
   if ((st = dev_alloc(p, &p->d_k, kvb, "device allocation of the K pool failed")) != PKV_OK) return st;
   if ((st = dev_alloc(p, &p->d_v, kvb, "device allocation of the V pool failed")) != PKV_OK) return st;
   if ((st = dev_alloc(p, (void**)&p->d_dk, grb, "device allocation of the dK pool failed")) != PKV_OK) return st;
@@ -113,6 +118,16 @@ pkv_status pool_allocate(pkv_pool* p) {
     if ((st = dev_alloc(p, (void**)&p->d_items, itemb, "device allocation of the window list failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_count, countb, "device allocation of the window list failed")) != PKV_OK) return st;
     if ((st = dev_alloc(p, (void**)&p->d_moved, 16, "device allocation of the copy counters failed")) != PKV_OK) return st;
+    if (with_stage) {
+      if ((st = dev_alloc(p, (void**)&p->d_stage, stageb, "device allocation of the writeback staging failed")) != PKV_OK)
+        return st;
+      p->stage_heads = stage_heads;
+      if ((e = hipEventCreateWithFlags(&p->ev_stage, hipEventDisableTiming)) != hipSuccess)
+        return pool_hip_fail(e, "hipEventCreate");
+      for (int w = 0; w < pkv_pool::kWindow; ++w)
+        if ((e = hipEventCreateWithFlags(&p->ev_count[w], hipEventDisableTiming)) != hipSuccess)
+          return pool_hip_fail(e, "hipEventCreate");
+    }
     for (int w = 0; w < pkv_pool::kWindow; ++w) {
       if ((e = hipEventCreateWithFlags(&p->ev_compute[w], hipEventDisableTiming)) != hipSuccess)
         return pool_hip_fail(e, "hipEventCreate");
@@ -164,6 +179,29 @@ pkv_status pool_allocate(pkv_pool* p) {
           return pool_fail(PKV_ENOMEM, "pinned host allocation of the staging page map failed");
         }
         p->host_bytes += need_w;
+        if (p->d_stage) {
+          const int64_t lb = p->stage_heads * (int64_t)sizeof(int2);
+          if (injected_failure(p))
+            return pool_fail(PKV_ENOMEM, "injected allocation failure (PKV_FAIL_ALLOC_AT)");
+          if ((e = hipHostMalloc((void**)&p->h_stage_items[w], (size_t)lb, hipHostMallocDefault)) !=
+              hipSuccess) {
+            p->h_stage_items[w] = nullptr;
+            (void)hipGetLastError();
+            return pool_fail(PKV_ENOMEM, "pinned host allocation of the staged page list failed");
+          }
+          p->host_bytes += lb;
+        }
+      }
+      if (p->d_stage) {
+        if (injected_failure(p))
+          return pool_fail(PKV_ENOMEM, "injected allocation failure (PKV_FAIL_ALLOC_AT)");
+        if ((e = hipHostMalloc((void**)&p->h_count, sizeof(int) * pkv_pool::kWindow,
+                               hipHostMallocDefault)) != hipSuccess) {
+          p->h_count = nullptr;
+          (void)hipGetLastError();
+          return pool_fail(PKV_ENOMEM, "pinned host allocation of the list lengths failed");
+        }
+        p->host_bytes += sizeof(int) * pkv_pool::kWindow;
       }
       try {
         p->adder = new HostAdder(host_add_threads());
@@ -185,10 +223,13 @@ pkv_status pool_release(pkv_pool* p) {
   delete p->adder;  // finishes the pending host adds
   p->adder = nullptr;
   for (int w = 0; w < pkv_pool::kWindow; ++w)
-    for (void* x : {p->h_stage_dk[w], p->h_stage_dv[w], (void*)p->h_stage_need[w]})
+    for (void* x : {p->h_stage_dk[w], p->h_stage_dv[w], (void*)p->h_stage_need[w],
+                    (void*)p->h_stage_items[w]})
       if (x) (void)hipHostFree(x);
+  if (p->h_count) (void)hipHostFree(p->h_count);
   void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_wtable,
-                 p->d_delta, p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved};
+                 p->d_delta, p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved,
+                 p->d_stage};
   for (void* x : dev)
     if (x) (void)hipFree(x);
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})
@@ -203,7 +244,9 @@ pkv_status pool_release(pkv_pool* p) {
     if (p->ev_wb[w]) (void)hipEventDestroy(p->ev_wb[w]);
     for (int b = 0; b < 2; ++b)
       if (p->ev_list[w][b]) (void)hipEventDestroy(p->ev_list[w][b]);
+    if (p->ev_count[w]) (void)hipEventDestroy(p->ev_count[w]);
   }
+  if (p->ev_stage) (void)hipEventDestroy(p->ev_stage);
   return st;
 }
 
@@ -365,6 +408,13 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
       (e = launch_need_mark(need, sel, d.n_kv_heads, d.max_logical_pages, n_pages, cs)) != hipSuccess ||
       (e = launch_window_list(p, layer, w, n_pages, cs)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: page map");
+  // the writeback sizes its staging copies by the list length
+  if (p->d_stage) {
+    if ((e = hipMemcpyAsync(p->h_count + w, p->d_count + (w * 2 + b), sizeof(int),
+                            hipMemcpyDeviceToHost, cs)) != hipSuccess ||
+        (e = hipEventRecord(p->ev_count[w], cs)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_prefetch_pages: list length");
+  }
   p->window_layer[w] = layer;
   p->window_grads[w] = with_grads;
   p->window_keys[w] = n_avail;
@@ -412,15 +462,32 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
     if ((e = p->adder->wait(p->stage_ticket[w])) != hipSuccess)
       return pool_hip_fail(e, "host gradient adds: hipEventSynchronize");
   }
-  if ((e = launch_writeback_pages(p, layer, w, cs)) != hipSuccess)
-    return pool_hip_fail(e, "pkv_writeback_grads: launch");
   const pkv_pool_desc& d = p->desc;
   const int64_t need_w = need_words(p);
   const int b = p->list_gen[w];
-  if (p->accumulate &&
-      (e = hipMemcpyAsync(p->h_stage_need[w], p->d_need + (int64_t)(w * 2 + b) * need_w,
-                          (size_t)need_w, hipMemcpyDeviceToHost, cs)) != hipSuccess)
-    return pool_hip_fail(e, "pkv_writeback_grads: page map copy");
+  int n_staged = 0;
+  if (p->d_stage) {
+    // the list length the prefetch copied (long since on the host), and the
+    // device staging once the previous staged writeback's copies read it
+    if ((e = hipEventSynchronize(p->ev_count[w])) != hipSuccess)
+      return pool_hip_fail(e, "hipEventSynchronize (window list length)");
+    n_staged = p->h_count[w];
+    n_staged = n_staged < 0 ? 0 : (n_staged > p->stage_heads ? (int)p->stage_heads : n_staged);
+    if (p->stage_recorded && (e = hipStreamWaitEvent(cs, p->ev_stage, 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (writeback staging)");
+    if ((e = launch_writeback_staged(p, w, n_staged, cs)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_writeback_grads: staging");
+    if ((e = hipEventRecord(p->ev_stage, cs)) != hipSuccess)
+      return pool_hip_fail(e, "hipEventRecord (writeback staging)");
+    p->stage_recorded = true;
+  } else {
+    if ((e = launch_writeback_pages(p, layer, w, cs)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_writeback_grads: launch");
+    if (p->accumulate &&
+        (e = hipMemcpyAsync(p->h_stage_need[w], p->d_need + (int64_t)(w * 2 + b) * need_w,
+                            (size_t)need_w, hipMemcpyDeviceToHost, cs)) != hipSuccess)
+      return pool_hip_fail(e, "pkv_writeback_grads: page map copy");
+  }
   if ((e = hipEventRecord(p->ev_list[w][b], cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (window list)");
   p->list_recorded[w][b] = true;
@@ -430,6 +497,10 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
   if (p->accumulate) {
     AddJob job;
     job.ready = p->ev_wb[w];
+    if (p->d_stage) {
+      job.list = p->h_stage_items[w];
+      job.n_list = n_staged;
+    }
     job.need = p->h_stage_need[w];
     const int32_t* tab = p->h_table.data() + (int64_t)layer * need_w;
     job.table.assign(tab, tab + need_w);

@@ -77,8 +77,9 @@ struct pkv_pool {
   unsigned long long* d_moved = nullptr;  // [0] bytes fetched, [1] bytes written back
 
   // host_grad_accumulate: window gradients start at zero on every prefetch;
-  // a writeback stages the visit's contributions (host gradient dtype,
-  // indexed like the tier) and the window's page map in pinned memory, and
+  // a writeback stages the visit's contributions (host gradient dtype) in
+  // pinned memory, in window-list order with the window list (device
+  // staging below) or indexed like the tier with the window's page map, and
   // `adder` adds them into the layer's host gradients.  stage_ticket[w] is
   // the add job that still reads window w's staging.
   bool accumulate = false;
@@ -88,6 +89,22 @@ struct pkv_pool {
   void* m_stage_dv[kWindow] = {nullptr, nullptr};
   uint8_t* h_stage_need[kWindow] = {nullptr, nullptr};
   int64_t stage_ticket[kWindow] = {0, 0};
+  // With room in the HBM budget, the writeback converts the visit's
+  // contributions into d_stage in window-list order (dK in the first
+  // stage_heads page-heads, dV in the next) and the DMA engine copies them,
+  // and the list, to the window's pinned staging in one piece each: the
+  // copy kernels' host writes would slow their own host reads on the link.
+  // d_stage == nullptr: the writeback kernel writes the pinned staging
+  // itself, indexed like the tier.  h_count[w] is the window list length of
+  // w's last prefetch (copied after the list is built, ev_count[w]);
+  // ev_stage follows the last staging copy, after which d_stage is free.
+  char* d_stage = nullptr;
+  int64_t stage_heads = 0;  // Hkv * window_slots
+  hipEvent_t ev_stage = nullptr;
+  bool stage_recorded = false;
+  int* h_count = nullptr;
+  hipEvent_t ev_count[kWindow] = {nullptr, nullptr};
+  int2* h_stage_items[kWindow] = {nullptr, nullptr};
   // the window's gradient pages still have to be zeroed: done on the stream
   // of the first attention backward (or writeback) of the visit, so that the
   // prefetch stream never waits for the window's previous writeback
@@ -142,6 +159,10 @@ hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
                         bool with_grads);
 hipError_t launch_window_grad_zero(const pkv_pool* p, int layer, int window, hipStream_t s);
 hipError_t launch_writeback_pages(const pkv_pool* p, int layer, int window, hipStream_t s);
+// Host accumulation with the device staging: the window list's first n
+// page-heads into d_stage (list order), then DMA copies of the staging and
+// the list to the window's pinned staging.
+hipError_t launch_writeback_staged(const pkv_pool* p, int window, int n, hipStream_t s);
 pkv_status pool_host_adds_wait(pkv_pool* p);
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,
                               hipStream_t s);

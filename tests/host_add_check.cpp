@@ -4,7 +4,9 @@
 // It drives the team the way the pool's writeback does: two staging areas
 // (one per window) used alternately, each refilled only after the add job
 // that last read it has finished; random page maps, random page tables,
-// random contributions.  The tier must end bit-identical to adding every
+// random contributions.  Every other job hands its page-heads as a list
+// (staging in list order, each entry naming its tier page-head, in a random
+// order), the others as a page map (staging indexed like the tier).  The tier must end bit-identical to adding every
 // job's contributions one job after the other, in submission order, with
 // round-to-nearest-even to bf16 (or fp32 adds).
 //
@@ -74,6 +76,7 @@ int main(int argc, char** argv) {
   }
   std::vector<uint8_t> need[2] = {std::vector<uint8_t>(hkv * max_logical),
                                   std::vector<uint8_t>(hkv * max_logical)};
+  std::vector<int2> list[2];
   std::normal_distribution<float> nd(0.f, 1.f);
   auto put = [&](std::vector<char>& b, int64_t i, float x) {
     if (bf16) {
@@ -113,22 +116,32 @@ int main(int argc, char** argv) {
         for (int j = 0; j < max_logical; ++j) table[g * max_logical + j] = perm[j];
       }
       const double density = 0.1 + 0.8 * (double)(rng() % 1000) / 1000.0;
+      const bool as_list = t % 4 >= 2;  // alternate per window
+      list[w].clear();
       for (int g = 0; g < hkv; ++g)
         for (int j = 0; j < max_logical; ++j) {
           const bool on = j < n_pages && (double)(rng() % 1000) / 1000.0 < density;
           need[w][g * max_logical + j] = on ? 1 : 0;
-          if (!on) continue;
-          const int64_t e0 = ((int64_t)g * slots + table[g * max_logical + j]) * page_elems;
-          for (int x = 0; x < 2; ++x)
-            for (int64_t e = 0; e < page_elems; ++e) {
-              put(stage[w][x], e0 + e, 0.25f * nd(rng));
-              // the serial reference: one rounded add per element and job
-              const float sum = get(expect[x], e0 + e) + get(stage[w][x], e0 + e);
-              put(expect[x], e0 + e, sum);
-            }
+          if (on) list[w].push_back(make_int2(g * slots + table[g * max_logical + j], 0));
         }
+      if (as_list) std::shuffle(list[w].begin(), list[w].end(), rng);
+      for (size_t i = 0; i < list[w].size(); ++i) {
+        const int64_t e0 = (int64_t)list[w][i].x * page_elems;         // tier
+        const int64_t s0 = as_list ? (int64_t)i * page_elems : e0;      // staging
+        for (int x = 0; x < 2; ++x)
+          for (int64_t e = 0; e < page_elems; ++e) {
+            put(stage[w][x], s0 + e, 0.25f * nd(rng));
+            // the serial reference: one rounded add per element and job
+            const float sum = get(expect[x], e0 + e) + get(stage[w][x], s0 + e);
+            put(expect[x], e0 + e, sum);
+          }
+      }
       pkv::AddJob job;
       job.ready = nullptr;
+      if (as_list) {
+        job.list = list[w].data();
+        job.n_list = (int)list[w].size();
+      }
       job.need = need[w].data();
       job.table = table;
       job.hkv = hkv;
