@@ -289,6 +289,39 @@ def test_host_accumulate_state_errors():
 SMALL = mini_config("qwen_1m_offload", n_ctx=8192, chunk=512, n_layers=2, top_k=6, slots=64)
 
 
+def test_host_adds_without_room_for_the_device_staging():
+    """Host adds with a device budget that holds the windows but not the
+    writeback's device staging: the pool is created without it (the writeback
+    kernel writes the pinned staging itself, indexed like the tier), its
+    device bytes are exactly the staging's fewer, and the sweep gives the
+    staged sweep's results: O, LSE, dQ and the selections bit-identical, dK/dV
+    within the bf16 bound of the staged sweep's and of the oracle."""
+    cfg = CFG
+    staged, g_staged, _, (dev_s, _, moved_s) = _sweep(cfg, True, accumulate=1, lookahead=True)
+    stage = 2 * cfg.hkv * cfg.n_pages * cfg.page * cfg.d * 2  # dK, dV of a window, bf16
+    tight = cfg.replace(hbm_cap_bytes=dev_s - stage)
+    plain, g_plain, _, (dev_p, _, moved_p) = _sweep(tight, True, accumulate=1, lookahead=True)
+    assert dev_p == dev_s - stage
+    assert moved_p == moved_s
+    for key in staged:
+        for name in ("O", "lse", "dq"):
+            assert np.array_equal(plain[key][name].numpy(), staged[key][name].numpy()), (key, name)
+        for x, y in zip(plain[key]["sel"], staged[key]["sel"]):
+            assert np.array_equal(x.numpy(), y.numpy())
+    for l in range(cfg.n_layers):
+        f = Workload(cfg, layer=l).full()
+        sels = [[[np.asarray(staged[(l, c)]["sel"][0][i, g, :staged[(l, c)]["sel"][1][i, g]]
+                  .numpy(), dtype=np.int64) for g in range(cfg.hkv)]
+                 for i in range(staged[(l, c)]["sel"][0].shape[0])] for c in range(cfg.n_chunks)]
+        ref = oracle.run_chunks(f.q, f.k, f.v, f.do, cfg.chunk, cfg.scale, cfg.page, sels=sels)
+        for which, i in (("dk", 0), ("dv", 1)):
+            e_pair = rel_err(g_plain[l][i], g_staged[l][i])
+            e_ref = rel_err(g_plain[l][i], ref[which])
+            print(f"layer {l} {which}: unstaged vs staged {e_pair:.2e}, vs oracle {e_ref:.2e}",
+                  flush=True)
+            assert e_pair < 1e-2 and e_ref < 1e-2
+
+
 @pytest.mark.parametrize("accumulate", [0, 1])
 def test_small_window_matches_resident_and_oracle(accumulate):
     """Windows of 36 slots per KV head for layers of 64 pages: each visit packs
