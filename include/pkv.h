@@ -97,8 +97,10 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *                prefetch places the page-heads it brings in the first free
  *                slots of its window, so the window bounds the pages one
  *                visit can hold, not the context: HBM use is then
- *                2 x Hkv x window_slots x P x d x (2 kv bytes + 8) plus the
- *                representatives and page tables, whatever
+ *                2 x Hkv x window_slots x P x d x (2 kv bytes + 8) (with
+ *                host_grad_accumulate, and room in the budget, plus the
+ *                writeback staging below) plus the representatives and
+ *                page tables, whatever
  *                max_logical_pages is ("Out of the Memory Barrier",
  *                gist.science de, section 4: memory grows by ~10 MB per 10K
  *                tokens; section 2.D: with page top-K only the selected
@@ -117,7 +119,14 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *                of K/V + gradients one way and gradients the other.  Costs
  *                pinned staging of two layers' dK/dV (host_grad_dtype) and,
  *                with bf16 host gradients, one more bf16 rounding per visit
- *                (contribution and sum are both rounded).  The adds finish
+ *                (contribution and sum are both rounded).  Where the
+ *                device budget leaves room, the writeback first gathers the
+ *                contributions into a device staging of
+ *                2 x Hkv x window_slots x P x d host-gradient elements, in
+ *                the order of the window's page list, and the DMA engine
+ *                copies them over the host link (the copy kernels' own host
+ *                writes would slow their host reads); without room, the
+ *                writeback kernel writes the pinned staging.  The adds finish
  *                asynchronously; every call that reads or zeroes the host
  *                gradients waits for them.  Thread count: environment
  *                variable PKV_HOST_ADD_THREADS, else min(16, CPUs the
