@@ -91,9 +91,10 @@ struct pkv_pool {
   int64_t stage_ticket[kWindow] = {0, 0};
   // With room in the HBM budget, the writeback converts the visit's
   // contributions into d_stage in window-list order (dK in the first
-  // stage_heads page-heads, dV in the next) and the DMA engine copies them,
-  // and the list, to the window's pinned staging in one piece each: the
-  // copy kernels' host writes would slow their own host reads on the link.
+  // stage_heads page-heads, dV in the next), and one runtime copy each
+  // (hipMemcpyAsync) moves them, and the list, to the window's pinned
+  // staging: contiguous copies slow the copy kernels' host reads on the
+  // link less than the kernels' own page-head writes to mapped host memory.
   // d_stage == nullptr: the writeback kernel writes the pinned staging
   // itself, indexed like the tier.  h_count[w] is the window list length of
   // w's last prefetch (copied after the list is built, ev_count[w]);
