@@ -685,8 +685,10 @@ def roofline_of(ktab: dict, workload: str) -> dict:
 def summarize_trace(trace_dir: str) -> dict:
     """Per-kernel totals and copy/compute overlap of a rocprofv3 kernel trace
     (--kernel-trace --output-format csv): for each host-link copy kernel
-    (fetch_kernel, writeback_kernel), the share of its duration during which
-    at least one other kernel runs, from the trace's start/end timestamps."""
+    (fetch_kernel, writeback_kernel, and the runtime's copy kernel that makes
+    the host-adds writeback's contiguous copies and the small list copies),
+    the share of its duration during which at least one other kernel runs,
+    from the trace's start/end timestamps."""
     import bisect
     import collections
     import csv
@@ -697,7 +699,7 @@ def summarize_trace(trace_dir: str) -> dict:
                 rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     if not rows:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    copy_names = ("fetch_kernel", "writeback_kernel")
+    copy_names = ("fetch_kernel", "writeback_kernel", "__amd_rocclr_copyBuffer")
 
     def copy_kind(n):
         return next((c for c in copy_names if c in n), None)

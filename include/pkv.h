@@ -124,10 +124,11 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *                contributions into a device staging of
  *                2 x Hkv x window_slots x P x d host-gradient elements, in
  *                the order of the window's page list, and one runtime copy
- *                per tensor moves them over the host link in one piece
- *                (the writeback kernel's page-head writes to mapped host
- *                memory slow the prefetch's host reads more); without room,
- *                the writeback kernel writes the pinned staging.  The adds finish
+ *                per tensor (hipMemcpyAsync, which the runtime makes on a
+ *                DMA engine) moves them over the host link: that slows the
+ *                prefetch's host reads far less than the writeback kernel's
+ *                writes to mapped host memory.  Without room, the writeback
+ *                kernel writes the pinned staging.  The adds finish
  *                asynchronously; every call that reads or zeroes the host
  *                gradients waits for them.  Thread count: environment
  *                variable PKV_HOST_ADD_THREADS, else min(16, CPUs the

@@ -250,8 +250,8 @@ __global__ void __launch_bounds__(256) writeback_kernel(
 // n listed page-heads (n = min(count, cap)) -> the staging in list order,
 // page-head i of the list to staging page-head i, in the host gradient
 // dtype (dK in the first cap page-heads, dV in the next).  HBM only, so a
-// full grid; one runtime copy per tensor then carries the staging over the
-// host link.
+// full grid; one runtime copy per tensor (on a DMA engine) then carries the
+// staging over the host link.
 __global__ void __launch_bounds__(256) stage_grads_kernel(
     const int2* __restrict__ items, const int* __restrict__ count, int cap, int64_t page_elems,
     bool grad_bf16, char* __restrict__ stage, const float* __restrict__ wdk,

@@ -92,9 +92,9 @@ struct pkv_pool {
   // With room in the HBM budget, the writeback converts the visit's
   // contributions into d_stage in window-list order (dK in the first
   // stage_heads page-heads, dV in the next), and one runtime copy each
-  // (hipMemcpyAsync) moves them, and the list, to the window's pinned
-  // staging: contiguous copies slow the copy kernels' host reads on the
-  // link less than the kernels' own page-head writes to mapped host memory.
+  // (hipMemcpyAsync, made on a DMA engine) moves them, and the list, to the
+  // window's pinned staging: that slows the copy kernels' host reads on the
+  // link far less than kernel writes to mapped host memory do.
   // d_stage == nullptr: the writeback kernel writes the pinned staging
   // itself, indexed like the tier.  h_count[w] is the window list length of
   // w's last prefetch (copied after the list is built, ev_count[w]);
