@@ -217,7 +217,16 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, int64_t pos0, int64_t n_
  *   o       device [n_q][n_q_heads][d], kv_dtype (written).
  *   lse     device [n_q_heads][n_q] fp32 (written), natural log.
  * Accumulation is fp32 (bf16 inputs go through bf16 MFMA with fp32
- * accumulate; fp32 inputs use fp32 arithmetic). */
+ * accumulate; fp32 inputs use fp32 arithmetic).  With a selection on a bf16
+ * pool, where every 128-row block of a head attends about as many keys, the
+ * last round of workgroups (when the blocks do not fill whole rounds of two
+ * per compute unit) is cut in two along the keys; each part's partial
+ * softmax state goes to a library-owned scratch buffer of the pool and a
+ * second kernel combines the parts (135 KB per split block; the buffer is
+ * grown with hipMalloc, after a device synchronisation, when a larger chunk
+ * arrives, so forward calls of one pool on different streams must not
+ * overlap, and a call under HIP graph capture needs an earlier call of at
+ * least the same size outside it). */
 pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n_q,
                         int32_t n_q_heads, float scale, const void* q, const pkv_sel* sel,
                         void* o, float* lse, hipStream_t stream);
@@ -427,8 +436,10 @@ pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* 
  * traffic alone.  bf16 pools without a host tier (else PKV_EUNSUPPORTED).
  *
  * pkv_measure_gather: streams into LDS exactly the K/V tiles that
- * pkv_attn_fwd(layer, q_pos0, n_q, n_q_heads, sel) reads (same grid, tile
- * walk, page-table lookups and double buffering; "Out of the Memory
+ * pkv_attn_fwd(layer, q_pos0, n_q, n_q_heads, sel) reads (same tile walk,
+ * page-table lookups and double buffering, and the forward's grid of one
+ * workgroup per 128 query rows and head; with a selection, the forward may
+ * cut its last round of workgroups in two, which this kernel does not; "Out of the Memory
  * Barrier", gist.science de, section 2.B: attention reads K/V page by page
  * through the table) and computes nothing.  out: caller-owned device buffer
  * of ceil(n_q / 128) * n_q_heads floats (one word per workgroup, contents

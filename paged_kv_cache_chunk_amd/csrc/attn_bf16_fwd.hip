@@ -10,20 +10,30 @@ namespace pkv {
 namespace {
 
 // NT: 32-row column tiles per wave (a wave owns 32*NT query rows);
-// BNT: keys per tile.  A workgroup owns 128 rows of one query head.
+// BNT: keys per tile.  A workgroup owns 128 rows of one query head: a whole
+// work unit, or one part of a tail-split unit (TailSplit).
 template <int NT, int BNT>
 __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2, 2))) fwd_bf16_kernel(AttnCall c, int n_qblocks) {
   constexpr int NW = 4 / NT;          // waves per workgroup
   constexpr int MT = BNT / 32;        // 32-key m-tiles per tile
   constexpr int TB = BNT * ROWB;      // bytes per K or V tile
+  static_assert(NT == 1, "the tail split's partial layout holds 32 rows per wave");
+  static_assert(BM == kFwdRows, "work unit rows");
   __shared__ __align__(1024) char sm[2][2 * TB];  // [buffer][K tile | V tile]
   const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  // Workgroup -> (query block, head): workgroups are dealt to the 8 XCDs
-  // round-robin, so bid % Hkv = KV head keeps every head's workgroups on the
+  // Workgroup -> work unit (and part): units [0, n_whole) first, then the
+  // first parts of the split units, then their second parts.
+  int bid = blockIdx.x, part = -1;
+  if (c.split.n_split > 0 && bid >= c.split.n_whole) {
+    const int j = bid - c.split.n_whole;
+    part = j >= c.split.n_split ? 1 : 0;
+    bid = c.split.n_whole + (part ? j - c.split.n_split : j);
+  }
+  // Work unit -> (query block, head): workgroups are dealt to the 8 XCDs
+  // round-robin, so unit % Hkv = KV head keeps every head's workgroups on the
   // same XCDs (sharing their L2 for that head's K/V); longest rows first.
   const int G = c.hq / c.g.hkv;
-  const int bid = blockIdx.x;
   const int g = uni(bid % c.g.hkv), m = uni(bid / c.g.hkv);
   const int qb = n_qblocks - 1 - m / G;
   const int h = g * G + m % G;
@@ -46,7 +56,7 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   }
 
   int n_tiles;
-  TileAhead<BNT> walk = make_ahead<BNT>(c, g, r0, rlast, &n_tiles);
+  TileAhead<BNT> walk = make_ahead<BNT>(c, g, r0, rlast, &n_tiles, part);
   TileDma<BNT, NW> dma;
   dma.init(w, lane);
   auto issue = [&](int b, const KeyTile& t, int slot) {
@@ -187,6 +197,28 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
     wait_dma_and_sync();
   }
 
+  if (part >= 0) {
+    // Store this part's partial, lane-major (each store instruction writes
+    // 1 KB of a wave): O as 16 float4 per lane, then m_ref and l_i per lane;
+    // fwd_merge_kernel combines the two parts.
+    const int s_unit = bid - c.split.n_whole;
+    float* mine = c.split.part + ((int64_t)(2 * s_unit + part) * NW + w) * kFwdPartWaveFloats;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        float4 v;
+        v.x = oacc[dt][0][4 * j4 + 0];
+        v.y = oacc[dt][0][4 * j4 + 1];
+        v.z = oacc[dt][0][4 * j4 + 2];
+        v.w = oacc[dt][0][4 * j4 + 3];
+        *reinterpret_cast<float4*>(mine + (dt * 4 + j4) * 256 + 4 * lane) = v;
+      }
+    mine[4096 + lane] = m_ref[0];
+    mine[4096 + 64 + lane] = l_i[0];
+    return;
+  }
+
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int my_r = rw0 + 32 * nt + l32;
@@ -209,12 +241,78 @@ __global__ void __launch_bounds__(256 / NT) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
+// One workgroup per split unit, its waves over the rows the forward's waves
+// own: the two parts' partials combined as the online softmax combines two
+// blocks of keys (both rescaled to the larger reference maximum), then O and
+// the log-sum-exp written as the forward writes them.  The parts are taken in
+// order (part 0's terms first), and the merge runs after the forward kernel
+// has finished, so its reads need no synchronisation of their own.
+__global__ void __launch_bounds__(256) fwd_merge_kernel(AttnCall c, int n_qblocks) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int s_unit = blockIdx.x;
+  const int unit = c.split.n_whole + s_unit;
+  const int G = c.hq / c.g.hkv;
+  const int g = unit % c.g.hkv, m = unit / c.g.hkv;
+  const int qb = n_qblocks - 1 - m / G;
+  const int h = g * G + m % G;
+  const int r0 = qb * BM;
+  const int rlast = (r0 + BM < c.n_q ? r0 + BM : c.n_q) - 1;
+  const float* p0 = c.split.part + ((int64_t)(2 * s_unit) * 4 + w) * kFwdPartWaveFloats;
+  const float* p1 = p0 + 4 * kFwdPartWaveFloats;
+  const float m0 = p0[4096 + lane], m1 = p1[4096 + lane];
+  const float mx = fmaxf(m0, m1);
+  const float base = mx == -INFINITY ? 0.f : mx;  // both parts empty: every weight 0
+  const float a0 = ex2(m0 - base), a1 = ex2(m1 - base);
+  const float l = p0[4096 + 64 + lane] * a0 + p1[4096 + 64 + lane] * a1;
+  const float lt = l + __shfl_xor(l, 32);
+  const int my_r = r0 + 32 * w + l32;
+  if (my_r > rlast) return;
+  const float inv = 1.f / lt;
+  u16* orow = reinterpret_cast<u16*>(c.o_out) + ((int64_t)my_r * c.hq + h) * D + 4 * half;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const float4 x = *reinterpret_cast<const float4*>(p0 + (dt * 4 + j4) * 256 + 4 * lane);
+      const float4 y = *reinterpret_cast<const float4*>(p1 + (dt * 4 + j4) * 256 + 4 * lane);
+      u32x2 v;
+      v.x = pack2((x.x * a0 + y.x * a1) * inv, (x.y * a0 + y.y * a1) * inv);
+      v.y = pack2((x.z * a0 + y.z * a1) * inv, (x.w * a0 + y.w * a1) * inv);
+      st8(orow + 32 * dt + 8 * j4, v);
+    }
+  if (half == 0) c.lse[(int64_t)h * c.n_q + my_r] = (mx + __log2f(lt)) * kLn2;
+}
+
 }  // namespace
+
+TailSplit plan_tail_split(int units, int slots) {
+  TailSplit sp;
+  if (slots <= 0 || units < slots) return sp;  // a single round (or less)
+  const int r = units % slots;
+  // no split when the last round is full or nearly so
+  if (r == 0 || 10 * r > 9 * slots) return sp;
+  sp.n_whole = units - r;
+  sp.n_split = r;
+  if (2 * r >= slots) {
+    sp.cut_num = r;
+    sp.cut_den = slots;
+  }
+  return sp;
+}
 
 hipError_t launch_fwd_bf16(const AttnCall& c, hipStream_t s) {
   const int nqb = (c.n_q + BM - 1) / BM;
-  KernelTimer t(KT_FWD, s);
-  hipLaunchKernelGGL((fwd_bf16_kernel<1, 64>), dim3(nqb * c.hq), dim3(256), 0, s, c, nqb);
+  const int units = nqb * c.hq;
+  if (c.split.n_split > 0 && (c.split.n_whole + c.split.n_split != units || !c.split.part ||
+                              c.split.cut_den <= 0))
+    return hipErrorInvalidValue;
+  const int grid = c.split.n_split > 0 ? units + c.split.n_split : units;
+  KernelTimer t(KT_FWD, s);  // the merge counts as part of the forward
+  hipLaunchKernelGGL((fwd_bf16_kernel<1, 64>), dim3(grid), dim3(256), 0, s, c, nqb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c.split.n_split == 0) return e;
+  hipLaunchKernelGGL(fwd_merge_kernel, dim3(c.split.n_split), dim3(256), 0, s, c, nqb);
   return hipGetLastError();
 }
 

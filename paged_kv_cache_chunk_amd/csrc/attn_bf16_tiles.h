@@ -329,11 +329,20 @@ struct TileAhead {
   }
 };
 
-// The look-ahead walker of a query block (the tiles of make_walk).
+// The look-ahead walker of a query block (the tiles of make_walk).  part 0 /
+// 1 of a tail-split unit: only the first floor(n cut_num / cut_den) of its n
+// tiles / the rest (*n_tiles is then the part's count).
 template <int BNT>
 __device__ __forceinline__ TileAhead<BNT> make_ahead(const AttnCall& c, int g, int r0, int rlast,
-                                                     int* n_tiles) {
+                                                     int* n_tiles, int part = -1) {
   const TileWalk<BNT> W = make_walk<BNT>(c, g, r0, rlast, n_tiles);
+  int t0 = 0;
+  if (part >= 0) {
+    const int n = *n_tiles;
+    const int cut = uni((int)((int64_t)n * c.split.cut_num / c.split.cut_den));
+    t0 = part ? cut : 0;
+    *n_tiles = part ? n - cut : cut;
+  }
   TileAhead<BNT> A;
   A.list = W.list;
   A.table = c.L.table + (int64_t)g * c.g.max_logical;
@@ -342,9 +351,10 @@ __device__ __forceinline__ TileAhead<BNT> make_ahead(const AttnCall& c, int g, i
   A.max_logical = W.max_logical;
   A.rel = W.rel;
   A.n_list = W.list ? uni(sel_count(c, r0 / c.g.page, g)) : 0;
-  A.pu = A.psub = 0;
-  A.lookup_list();  // tile 0
-  A.advance();      // tile 0 next (slot loading), tile 1's list entry loading
+  A.pu = uni(t0 / W.tpp);
+  A.psub = uni(t0 % W.tpp);
+  A.lookup_list();  // tile t0
+  A.advance();      // tile t0 next (slot loading), tile t0 + 1's list entry loading
   return A;
 }
 

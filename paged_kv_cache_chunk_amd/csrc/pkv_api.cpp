@@ -390,6 +390,17 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   c.q = q;
   c.o_out = o;
   c.lse = lse;
+  if (sel && pool->desc.kv_dtype == PKV_BF16) {
+    // top-K: every unit attends about as many keys; split the last round
+    const int slots = 2 * pool->n_cus;
+    TailSplit sp = plan_tail_split((int)cdiv(n_q, kFwdRows) * n_q_heads, slots);
+    if (sp.n_split > 0) {
+      const int64_t need = (int64_t)sp.n_split * 2 * 4 * kFwdPartWaveFloats * 4;
+      if ((st = ensure_scratch(&pool->d_fsplit, &pool->fsplit_bytes, need)) != PKV_OK) return st;
+      sp.part = (float*)pool->d_fsplit;
+      c.split = sp;
+    }
+  }
   hipError_t e = pool->desc.kv_dtype == PKV_BF16 ? launch_fwd_bf16(c, stream) : launch_fwd_f32(c, stream);
   if (e != hipSuccess) return hip_fail(e, "pkv_attn_fwd: launch");
   return pool_after_compute(pool, layer, stream);

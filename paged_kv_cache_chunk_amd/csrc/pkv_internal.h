@@ -53,6 +53,37 @@ struct DkvPlan {
   int64_t bytes;
 };
 
+// Tail split of a bf16 forward launch whose work units (128 query rows of one
+// head) all cost about the same, as in top-K mode, where every query page
+// attends the same number of pages.  The kernel fits two workgroups on a CU,
+// so U units on S = 2 x CUs slots take ceil(U / S) rounds of work although
+// they hold U / S: with U = q S + r, the last round leaves S - r slots idle.
+// The last r units are therefore cut in two along their key tiles, a first
+// part with the fraction cut_num / cut_den of the tiles (r / S, or 1/2 when
+// r < S / 2) and a second part with the rest.  Dispatched after the q S whole
+// units, the r first parts take r slots while the other S - r slots run the r
+// second parts, so every slot finishes after about q + r / S units.  Each
+// part stores its partial result (O unnormalised, the reference maximum and
+// the row sums); a second kernel combines the two parts of every split unit
+// and writes its O and log-sum-exp.
+struct TailSplit {
+  int n_whole = 0;   // units [0, n_whole) run whole
+  int n_split = 0;   // units [n_whole, n_whole + n_split) run in two parts; 0: no split
+  int cut_num = 1, cut_den = 2;
+  float* part = nullptr;  // [n_split][2 parts][4 waves][kFwdPartWaveFloats]
+};
+
+// Query rows of one bf16 forward work unit (one workgroup, four waves).
+constexpr int kFwdRows = 128;
+
+// Floats of one wave's partial forward result: O (32 rows x 128 columns),
+// then the reference maximum and the row sum of each of its 64 lanes.
+constexpr int kFwdPartWaveFloats = 32 * 128 + 2 * 64;
+
+// The split of a forward launch of `units` work units on a device with
+// `slots` workgroup slots (part left unset).
+TailSplit plan_tail_split(int units, int slots);
+
 // Everything an attention launch needs.
 struct AttnCall {
   LayerDev L;
@@ -72,6 +103,7 @@ struct AttnCall {
   float* lse2;   // lse * log2(e), [hq][n_q] (bf16 backward only)
   float* dq;
   DkvPlan plan;  // sparse bf16 backward only
+  TailSplit split;  // sparse bf16 forward only
 };
 
 // Whether kernel timing (pkv_kernel_timing) is on.

@@ -109,6 +109,10 @@ pkv_status pool_allocate(pkv_pool* p) {
   if (e != hipSuccess) return pool_hip_fail(e, "hipMemcpy (page tables)");
   if ((e = hipStreamCreateWithFlags(&p->s_aux, hipStreamNonBlocking)) != hipSuccess)
     return pool_hip_fail(e, "hipStreamCreate");
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess ||
+      (e = hipDeviceGetAttribute(&p->n_cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return pool_hip_fail(e, "hipDeviceGetAttribute (compute units)");
   if ((e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming)) != hipSuccess ||
       (e = hipEventCreateWithFlags(&p->ev_join, hipEventDisableTiming)) != hipSuccess)
     return pool_hip_fail(e, "hipEventCreate");
@@ -228,8 +232,8 @@ pkv_status pool_release(pkv_pool* p) {
       if (x) (void)hipHostFree(x);
   if (p->h_count) (void)hipHostFree(p->h_count);
   void* dev[] = {p->d_k, p->d_v, p->d_dk, p->d_dv, p->d_reps, p->d_table, p->d_wtable,
-                 p->d_delta, p->d_select, p->d_need, p->d_items, p->d_count, p->d_moved,
-                 p->d_stage};
+                 p->d_delta, p->d_select, p->d_fsplit, p->d_need, p->d_items, p->d_count,
+                 p->d_moved, p->d_stage};
   for (void* x : dev)
     if (x) (void)hipFree(x);
   for (auto* v : {&p->h_k, &p->h_v, &p->h_dk, &p->h_dv})

@@ -42,6 +42,10 @@ struct pkv_pool {
   int64_t delta_bytes = 0;
   void* d_select = nullptr;       // select scratch
   int64_t select_bytes = 0;
+  // bf16 top-K forward: partial results of the tail split's parts
+  void* d_fsplit = nullptr;
+  int64_t fsplit_bytes = 0;
+  int n_cus = 0;                  // compute units of the pool's device
   int64_t device_bytes = 0;
   int64_t host_bytes = 0;
   int allocs = 0;  // allocations made so far by pool creation (failure-injection hook)

@@ -30,6 +30,10 @@ CASES = {
     "bf16_topk": (lambda: mini_config("qwen_256k_topk", n_ctx=5 * 1024 + 200, chunk=1024,
                                       top_k=4), 4),
     "f32_topk": (lambda: get_config("tiny_f32"), 2),
+    # a last chunk of 28 query blocks x 28 heads: on a 256-CU device the
+    # forward splits its last round of workgroups and adds a merge kernel
+    "bf16_topk_split": (lambda: mini_config("qwen_256k_topk", n_ctx=2 * 3584, chunk=3584,
+                                            top_k=6), 6),
 }
 
 
@@ -94,8 +98,8 @@ def test_graph_replays_match_eager_calls(case):
             sel[0].fill_(-7)
             sel[1].fill_(-7)
 
-    # eager reference (this call also sizes the selection's scratch, so that
-    # nothing grows under capture)
+    # eager reference (this call also sizes the selection's scratch and the
+    # forward's split scratch, so that nothing grows under capture)
     pkv.pkv_grad_zero(pool, 0)
     poison()
     calls()

@@ -204,6 +204,49 @@ def test_bf16_other_shapes(hq, hkv, page, sparse_k):
     _check(cfg, got, ref, TOL["bf16"])
 
 
+def _split_plan(units: int):
+    """The forward's tail split on this device (two workgroups per compute
+    unit): (units split in two, first part's fraction of the key tiles)."""
+    import torch
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    if units < slots:
+        return 0, None
+    r = units % slots
+    if r == 0 or 10 * r > 9 * slots:
+        return 0, None
+    return r, (r / slots if 2 * r >= slots else 0.5)
+
+
+@pytest.mark.parametrize("n_ctx,chunk,top_k", [
+    (7168, 3584, 6),   # 2 chunks of 28 query blocks x 28 heads: 784 units, the last 272 split (cut 272/512)
+    (2600, 2688, 3),   # one chunk of 21 query blocks (ragged last one): 588 units, 76 split in halves
+])
+def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k):
+    """Top-K chunks large enough that the bf16 forward cuts its last round of
+    work units in two parts along their key tiles (every unit attends about
+    as many keys, so a partial last round would leave slots idle): each part
+    keeps a partial softmax state and a second kernel combines the two.  O,
+    LSE, dQ, dK, dV against the oracle, every element; and a second run
+    bit-identical."""
+    from paged_kv_cache_chunk_amd.chunks import Sparse
+    cfg = mini_config("qwen_256k_topk", n_ctx=n_ctx, chunk=chunk, top_k=top_k)
+    plans = [_split_plan(-(-cfg.chunk_range(c)[1] // 128) * cfg.hq) for c in range(cfg.n_chunks)]
+    print(f"splits per chunk: {plans}", flush=True)
+    if not any(n for n, _ in plans):
+        pytest.skip("no chunk of this case has a split last round on this device")
+    sp = Sparse(top_k=top_k)
+    w = Workload(cfg)
+    got = run_layer(cfg, w, sparse=sp)
+    again = run_layer(cfg, w, sparse=sp)
+    for name in ("O", "lse", "dq"):
+        assert np.array_equal(got[name], again[name]), name
+    f, ref = _oracle_for(cfg, w, sp)
+    ref = _check_sel(cfg, f, got, ref, sp)
+    _check(cfg, got, ref, TOL["bf16"])
+    got["pool"].close()
+    again["pool"].close()
+
+
 def test_bf16_sparse_chunk_over_64_query_pages():
     """A top-K chunk of 71 query pages: the sparse dK/dV work items carry the
     first two 32-bit words of their key page's query-page mask and the kernel
