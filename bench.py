@@ -766,8 +766,8 @@ def summarize_counters(fetch_dir: str, write_dir: str, cal_fetch_dir: str, cal_w
     ff = cal_bytes / 1024 / (sum(cf[ck]) / len(cf[ck]))
     wf = cal_bytes / 1024 / (sum(cw[ck]) / len(cw[ck]))
     f, w = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
-    names = {"fwd": "fwd_bf16_kernel", "dq": "dq_bf16_kernel", "dkdv": "dkdv_bf16_kernel",
-             "gather": "gather_kernel", "atomics": "atomics_kernel"}
+    names = {"fwd": "fwd_bf16_kernel", "fwd_merge": "fwd_merge_kernel", "dq": "dq_bf16_kernel",
+             "dkdv": "dkdv_bf16_kernel", "gather": "gather_kernel", "atomics": "atomics_kernel"}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     data.update({"_doc": "HBM bytes per launch = FETCH_SIZE*fetch_factor + WRITE_SIZE*write_factor "
