@@ -165,9 +165,4 @@ hipError_t launch_micro_atomics(const AttnCall& c, int reps, float value, hipStr
 // ---- kernels in attn_common.hip
 hipError_t launch_delta(const AttnCall& c, bool bf16, hipStream_t s);
 
-// ---- host tier (offload.hip)
-hipError_t launch_gather_host_pages(const void* host_base, void* dev_base,
-                                    const int32_t* page_list, const int32_t* n_list,
-                                    int64_t page_bytes, int64_t max_pages, hipStream_t s);
-
 }  // namespace pkv
