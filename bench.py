@@ -346,12 +346,15 @@ def block_bench(n_ctx: int, chunk: int, top_k: int = 0) -> dict:
             "forward_sweep_working_set_bytes": ws_fwd, "backward_sweep_working_set_bytes": ws_bwd}
 
 
-def stack_bench(n_layers: int, n_ctx: int, chunk: int, top_k: int = 0) -> dict:
+def stack_bench(n_layers: int, n_ctx: int, chunk: int, top_k: int = 0,
+                host_grads: str = "f32", host_adds: bool = False) -> dict:
     """Chunk-recurrent training of a stack of n_layers random-initialised
     Qwen2.5-7B-shaped attention blocks (hidden 3584, Hq 28, Hkv 4, d 128),
     once with every pool in HBM and once with every layer's K/V (bf16) and
-    KV gradients (fp32) in pinned host memory and two HBM windows filled one
-    layer ahead on a side stream.  Reports each sweep's time, the overhead of
+    KV gradients (host_grads: fp32 or bf16) in pinned host memory and two HBM
+    windows filled one layer ahead on a side stream (host_adds: gradient
+    contributions added into the host tier by the library's host threads, so
+    the backward fetches K/V only).  Reports each sweep's time, the overhead of
     the host tier, the copy kernels' time and the share of it hidden behind
     compute (copy time minus the added wall time, over copy time), and the
     HBM and pinned bytes of the pools."""
@@ -360,11 +363,14 @@ def stack_bench(n_layers: int, n_ctx: int, chunk: int, top_k: int = 0) -> dict:
     from paged_kv_cache_chunk_amd.chunks import Sparse
     from paged_kv_cache_chunk_amd.recurrent import AttentionStack
 
-    out = {"layers": n_layers, "context": n_ctx, "chunk": chunk, "top_k": top_k or None}
+    out = {"layers": n_layers, "context": n_ctx, "chunk": chunk, "top_k": top_k or None,
+           "host_grad_dtype": host_grads, "host_grad_accumulate": int(host_adds)}
     for mode in ("resident", "host_tier"):
         torch.cuda.empty_cache()
         st = AttentionStack(n_layers, max_tokens=n_ctx, sparse=Sparse(top_k) if top_k else None,
-                            seed=0, host_tier=mode == "host_tier")
+                            seed=0, host_tier=mode == "host_tier",
+                            host_grad_dtype=pkv.PKV_BF16 if host_grads == "bf16" else pkv.PKV_F32,
+                            host_grad_accumulate=host_adds)
         g = torch.Generator(device="cuda")
         g.manual_seed(11)
         xs, gys = [], []
@@ -825,6 +831,11 @@ def main():
                          "--stack-chunk, --block-top-k)")
     ap.add_argument("--stack-ctx", type=int, default=131072)
     ap.add_argument("--stack-chunk", type=int, default=12288)
+    ap.add_argument("--stack-host-grads", choices=("f32", "bf16"), default="f32",
+                    help="element type of the host tier's KV gradients in --stack")
+    ap.add_argument("--stack-host-adds", type=int, default=0,
+                    help="1: --stack adds the gradient contributions on the host "
+                         "(host_grad_accumulate)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (reference "
                          "for the profiler's FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -870,7 +881,8 @@ def main():
         sys.exit(1)
 
     if args.stack:
-        r = stack_bench(args.stack, args.stack_ctx, args.stack_chunk, args.block_top_k)
+        r = stack_bench(args.stack, args.stack_ctx, args.stack_chunk, args.block_top_k,
+                        args.stack_host_grads, bool(args.stack_host_adds))
         print(json.dumps({"metric": "chunk-recurrent attention-stack training: host tier vs HBM",
                           "n_gpus": 1, "dtype": "bf16", "data": "synthetic", **r}), flush=True)
         return

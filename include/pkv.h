@@ -390,9 +390,12 @@ pkv_status pkv_read_pages(pkv_pool* pool, int32_t layer, int32_t what, void* dst
  * when the window holds no gradients of the layer) and their pages must be
  * among those it fetched: a chunk's own pages are, for any selection of
  * pkv_select_topk_pages (its query page is always kept) and for a prefix
- * prefetch up to the chunk's end.  The dK/dV read there are the window's:
- * the accumulated sums when the prefetch fetched them, or only this visit's
- * contributions with host_grad_accumulate. */
+ * prefetch up to the chunk's end.  dK/dV are the accumulated sums: the
+ * window's when the prefetch fetched them; with host_grad_accumulate the
+ * window's contributions of this visit plus the host tier's sums of the
+ * earlier ones (the call first waits on the host for the adds of the
+ * layer's last writeback, then reads the tier rows through its device-mapped
+ * alias). */
 pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t pos0,
                          int64_t n_tok, void* dst, hipStream_t stream);
 

@@ -307,6 +307,50 @@ __global__ void export_bf16_grad_kernel(const unsigned short* __restrict__ src,
   }
 }
 
+// dst[t][g][:] (fp32) = window gradient + host-tier gradient of token
+// t0 + t: the complete sum of a gradient row while the host adds the window's
+// contributions into the tier (host_grad_accumulate).  Four elements per
+// thread; the tier is read through its device-mapped alias (bf16 or fp32).
+__global__ void grad_rows_sum_kernel(const float* __restrict__ win, const int32_t* __restrict__ wtab,
+                                     int wslots, const void* __restrict__ tier,
+                                     const int32_t* __restrict__ ttab, int tslots, bool tier_bf16,
+                                     float* __restrict__ dst, int hkv, int page, int max_logical,
+                                     int d, int64_t t0, int64_t n_tok) {
+  const int q = d / 4;
+  const int64_t total = n_tok * hkv * q;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int e = 4 * (int)(idx % q);
+    const int64_t tg = idx / q;
+    const int g = (int)(tg % hkv);
+    const int64_t t = t0 + tg / hkv;
+    const int64_t pg = t / page;
+    const int64_t row = t % page;
+    const int64_t wo = (((int64_t)g * wslots + wtab[(int64_t)g * max_logical + pg]) * page + row) * d + e;
+    const int64_t to = (((int64_t)g * tslots + ttab[(int64_t)g * max_logical + pg]) * page + row) * d + e;
+    float4 a = *reinterpret_cast<const float4*>(win + wo);
+    float b[4];
+    if (tier_bf16) {
+      const uint2 u = *reinterpret_cast<const uint2*>((const unsigned short*)tier + to);
+      b[0] = __uint_as_float(u.x << 16);
+      b[1] = __uint_as_float(u.x & 0xffff0000u);
+      b[2] = __uint_as_float(u.y << 16);
+      b[3] = __uint_as_float(u.y & 0xffff0000u);
+    } else {
+      const float4 v = *reinterpret_cast<const float4*>((const float*)tier + to);
+      b[0] = v.x;
+      b[1] = v.y;
+      b[2] = v.z;
+      b[3] = v.w;
+    }
+    a.x += b[0];
+    a.y += b[1];
+    a.z += b[2];
+    a.w += b[3];
+    *reinterpret_cast<float4*>(dst + tg * d + e) = a;
+  }
+}
+
 int grid_of(int64_t work) {
   int64_t b = (work + 255) / 256;
   if (b > 65536) b = 65536;
@@ -436,6 +480,24 @@ hipError_t launch_writeback_staged(const pkv_pool* p, int window, int n, hipStre
     return e;
   return hipMemcpyAsync(p->h_stage_items[window], L.items, (size_t)n * sizeof(int2),
                         hipMemcpyDeviceToHost, s);
+}
+
+hipError_t launch_grad_rows_sum(const pkv_pool* p, int layer, int what, int64_t t0, int64_t n_tok,
+                                float* dst, hipStream_t s) {
+  const pkv_pool_desc& d = p->desc;
+  if (n_tok <= 0) return hipSuccess;
+  if (d.head_dim % 4) return hipErrorInvalidValue;
+  const int64_t tab_stride = (int64_t)d.n_kv_heads * d.max_logical_pages;
+  const int w = p->window_of(layer);
+  const float* win = (what == PKV_DK ? p->d_dk : p->d_dv) + (int64_t)w * p->dev_elems;
+  const int32_t* wtab = p->d_wtable + w * tab_stride;
+  const void* tier = what == PKV_DK ? p->m_dk[layer] : p->m_dv[layer];
+  const int32_t* ttab = p->d_table + (int64_t)layer * tab_stride;
+  hipLaunchKernelGGL(grad_rows_sum_kernel, dim3(grid_of(n_tok * d.n_kv_heads * (d.head_dim / 4))),
+                     dim3(256), 0, s, win, wtab, p->window_slots, tier, ttab, d.n_slots,
+                     d.host_grad_dtype == PKV_BF16, dst, d.n_kv_heads, d.page_size,
+                     d.max_logical_pages, d.head_dim, t0, n_tok);
+  return hipGetLastError();
 }
 
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,

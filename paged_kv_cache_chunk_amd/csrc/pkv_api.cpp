@@ -160,6 +160,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
                      ? (int64_t)d.n_kv_heads * p->window_slots * d.page_size * d.head_dim
                      : p->layer_elems;
   p->length.assign(d.n_layers, 0);
+  p->layer_ticket.assign(d.n_layers, 0);
   p->h_table.resize((size_t)d.n_layers * d.n_kv_heads * d.max_logical_pages);
   for (int l = 0; l < d.n_layers; ++l)
     for (int g = 0; g < d.n_kv_heads; ++g)
@@ -507,8 +508,17 @@ pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t po
     const bool grads = what == PKV_DK || what == PKV_DV;
     pkv_status st = pool_before_compute(pool, layer, pos0 + n_tok, stream, grads);
     if (st != PKV_OK) return st;
-    hipError_t e = launch_export(layer_view(pool, layer), compute_geom(pool), what, pool->kv_bytes,
-                                 n_tok, dst, stream, pos0);
+    hipError_t e;
+    if (grads && pool->accumulate) {
+      // the window holds this visit's contributions; the tier the sums of
+      // the earlier visits once their host adds have run
+      if ((e = pool->adder->wait(pool->layer_ticket[layer])) != hipSuccess)
+        return hip_fail(e, "pkv_read_rows: host gradient adds");
+      e = launch_grad_rows_sum(pool, layer, what, pos0, n_tok, (float*)dst, stream);
+    } else {
+      e = launch_export(layer_view(pool, layer), compute_geom(pool), what, pool->kv_bytes, n_tok,
+                        dst, stream, pos0);
+    }
     if (e != hipSuccess) return hip_fail(e, "pkv_read_rows: launch");
     return pool_after_compute(pool, layer, stream);
   }

@@ -519,6 +519,7 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
     job.dst_dk = p->h_dk[layer];
     job.dst_dv = p->h_dv[layer];
     p->stage_ticket[w] = p->adder->submit(job);
+    p->layer_ticket[layer] = p->stage_ticket[w];
     p->window_grads[w] = false;  // a second writeback would add the same contributions again
   }
   if (done && (e = hipEventRecord(done, cs)) != hipSuccess)

@@ -93,6 +93,7 @@ struct pkv_pool {
   void* m_stage_dv[kWindow] = {nullptr, nullptr};
   uint8_t* h_stage_need[kWindow] = {nullptr, nullptr};
   int64_t stage_ticket[kWindow] = {0, 0};
+  std::vector<int64_t> layer_ticket;  // per layer: ticket of its last add job (0: none)
   // With room in the HBM budget, the writeback converts the visit's
   // contributions into d_stage in window-list order (dK in the first
   // stage_heads page-heads, dV in the next), and one runtime copy each
@@ -171,5 +172,10 @@ hipError_t launch_writeback_staged(const pkv_pool* p, int window, int n, hipStre
 pkv_status pool_host_adds_wait(pkv_pool* p);
 hipError_t launch_host_export(const pkv_pool* p, int layer, int what, int64_t n_tok, void* dst,
                               hipStream_t s);
+// host_grad_accumulate: rows [t0, t0 + n_tok) of the layer's dK or dV as
+// the window's contributions plus the host tier's sums (fp32 out); the host
+// adds of the layer's earlier writebacks must have run.
+hipError_t launch_grad_rows_sum(const pkv_pool* p, int layer, int what, int64_t t0, int64_t n_tok,
+                                float* dst, hipStream_t s);
 
 }  // namespace pkv

@@ -187,7 +187,11 @@ class AttentionStack:
     attention run (de 2.C: prefetch of the next layer; with sparse attention
     the transfer overlaps the K/V projections); the backward's fetches bring
     the pages' accumulated gradients, and a third stream writes each layer's
-    gradient pages back after its backward.  In the forward sweep of a dense
+    gradient pages back after its backward.  With host_grad_accumulate the
+    backward's fetches bring K/V only: the window's gradients start at zero,
+    the writeback sends the visit's contributions, and the library's host
+    threads add them into the host tier (the chunk's own dK/dV rows are then
+    read as window plus tier).  In the forward sweep of a dense
     stack the next layer's prefix is fetched before its chunk is appended
     (the append then writes the window too); in top-K mode a layer's
     selection needs its chunk's page representatives, so its fetch waits for
@@ -199,12 +203,13 @@ class AttentionStack:
                  max_tokens: int = 131072, sparse: Optional[Sparse] = None,
                  dtype: torch.dtype = torch.bfloat16, seed: int = 0, device: str = "cuda",
                  host_tier: bool = False, host_grad_dtype: int = PKV_F32,
-                 window_slots: int = 0):
+                 window_slots: int = 0, host_grad_accumulate: bool = False):
         pages = -(-max_tokens // page)
         kvd = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
         self.pool = pkv_pool_create(n_layers, hkv, d, page, pages, pages, kvd,
                                     host_tier=int(host_tier), host_grad_dtype=host_grad_dtype,
-                                    window_slots=window_slots if host_tier else 0)
+                                    window_slots=window_slots if host_tier else 0,
+                                    host_grad_accumulate=int(host_tier and host_grad_accumulate))
         self.blocks = [AttentionBlock(hidden, hq, hkv, d, rope_base, page, max_tokens, sparse,
                                       dtype, seed + l, device, pool=self.pool, layer=l)
                        for l in range(n_layers)]

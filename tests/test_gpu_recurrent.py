@@ -127,13 +127,13 @@ def test_recurrent_block_top_k_matches_reference():
     block.close()
 
 
-def _stack_run(dtype, sparse, host_tier, n_ctx=1536, chunk=512, layers=2):
+def _stack_run(dtype, sparse, host_tier, n_ctx=1536, chunk=512, layers=2, host_adds=False):
     from paged_kv_cache_chunk_amd.chunks import Sparse
     from paged_kv_cache_chunk_amd.recurrent import AttentionStack
     torch.manual_seed(3)
     st = AttentionStack(layers, hidden=256, hq=4, hkv=2, d=128, page=128, max_tokens=n_ctx,
                         sparse=Sparse(top_k=3) if sparse else None, dtype=dtype, seed=5,
-                        host_tier=host_tier)
+                        host_tier=host_tier, host_grad_accumulate=host_adds)
     x = torch.randn(n_ctx, 256, device="cuda")
     gy = torch.randn(n_ctx, 256, device="cuda") / 16
     xs = [x[i:i + chunk].to(dtype) for i in range(0, n_ctx, chunk)]
@@ -147,15 +147,20 @@ def _stack_run(dtype, sparse, host_tier, n_ctx=1536, chunk=512, layers=2):
     return out
 
 
+@pytest.mark.parametrize("host_adds", [False, True])
 @pytest.mark.parametrize("sparse", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_stack_host_tier_matches_resident(sparse, dtype):
+def test_stack_host_tier_matches_resident(sparse, dtype, host_adds):
     """A two-layer stack with every layer's K/V and KV gradients in the host
     tier (fp32 host gradients; two HBM windows filled one layer ahead on a
     side stream; in dense mode the forward sweep fetches a layer before its
     chunk is appended) gives the outputs of the all-HBM stack bit for bit and
-    its gradients up to the order of the fp32 atomic adds."""
-    off = _stack_run(dtype, sparse, True)
+    its gradients up to the order of the fp32 additions.  host_adds: the
+    backward fetches K/V only and the library's host threads add each visit's
+    gradient contributions into the tier; the chunk's own dK/dV rows, which
+    go back through W_k and W_v, are then the window's contributions plus the
+    tier's sums."""
+    off = _stack_run(dtype, sparse, True, host_adds=host_adds)
     res = _stack_run(dtype, sparse, False)
     assert torch.equal(off["y"], res["y"])
 
@@ -165,7 +170,7 @@ def test_stack_host_tier_matches_resident(sparse, dtype):
     errs = {"dx": rel(off["dx"], res["dx"])}
     for i, (a, b) in enumerate(zip(off["dw"], res["dw"])):
         errs[f"dw{i}"] = rel(a, b)
-    print(dtype, sparse, {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    print(dtype, sparse, host_adds, {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
     for k, e in errs.items():
         assert e <= tol, (k, e)
     off["st"].close()
