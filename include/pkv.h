@@ -130,7 +130,8 @@ typedef struct pkv_pool pkv_pool; /* opaque; owned by the library */
  *                writes to mapped host memory.  Without room, the writeback
  *                kernel writes the pinned staging.  The adds finish
  *                asynchronously; every call that reads or zeroes the host
- *                gradients waits for them.  Thread count: environment
+ *                gradients waits for them (pkv_read_rows of dK/dV returns
+ *                the window's contributions plus the tier's sums).  Thread count: environment
  *                variable PKV_HOST_ADD_THREADS, else min(16, CPUs the
  *                process may run on).
  *   device_budget_bytes  host-tier only: cap on the library's HBM use; pool
