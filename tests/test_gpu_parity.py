@@ -217,11 +217,12 @@ def _split_plan(units: int):
     return r, (r / slots if 2 * r >= slots else 0.5)
 
 
-@pytest.mark.parametrize("n_ctx,chunk,top_k", [
-    (7168, 3584, 6),   # 2 chunks of 28 query blocks x 28 heads: 784 units, the last 272 split (cut 272/512)
-    (2600, 2688, 3),   # one chunk of 21 query blocks (ragged last one): 588 units, 76 split in halves
+@pytest.mark.parametrize("n_ctx,chunk,top_k,page", [
+    (7168, 3584, 6, 128),  # 2 chunks of 28 query blocks x 28 heads: 784 units, the last 272 split (cut 272/512)
+    (2600, 2688, 3, 128),  # one chunk of 21 query blocks (ragged last one): 588 units, 76 split in halves
+    (2816, 2816, 3, 256),  # pages of 256 (4 key tiles each, a part may start inside a page): 616 units, 104 split
 ])
-def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k):
+def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k, page):
     """Top-K chunks large enough that the bf16 forward cuts its last round of
     work units in two parts along their key tiles (every unit attends about
     as many keys, so a partial last round would leave slots idle): each part
@@ -229,7 +230,7 @@ def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k):
     LSE, dQ, dK, dV against the oracle, every element; and a second run
     bit-identical."""
     from paged_kv_cache_chunk_amd.chunks import Sparse
-    cfg = mini_config("qwen_256k_topk", n_ctx=n_ctx, chunk=chunk, top_k=top_k)
+    cfg = mini_config("qwen_256k_topk", n_ctx=n_ctx, chunk=chunk, top_k=top_k, page=page)
     plans = [_split_plan(-(-cfg.chunk_range(c)[1] // 128) * cfg.hq) for c in range(cfg.n_chunks)]
     print(f"splits per chunk: {plans}", flush=True)
     if not any(n for n, _ in plans):
