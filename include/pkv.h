@@ -220,7 +220,7 @@ pkv_status pkv_append_kv(pkv_pool* pool, int32_t layer, int64_t pos0, int64_t n_
  * Accumulation is fp32 (bf16 inputs go through bf16 MFMA with fp32
  * accumulate; fp32 inputs use fp32 arithmetic).  With a selection on a bf16
  * pool, where every 128-row block of a head attends about as many keys, the
- * last round of workgroups (when the blocks do not fill whole rounds of two
+ * last pass of workgroups (when the blocks do not fill whole passes of two
  * per compute unit) is cut in two along the keys; each part's partial
  * softmax state goes to a library-owned scratch buffer of the pool and a
  * second kernel combines the parts (135 KB per split block; the buffer is
@@ -443,7 +443,7 @@ pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* 
  * pkv_attn_fwd(layer, q_pos0, n_q, n_q_heads, sel) reads (same tile walk,
  * page-table lookups and double buffering, and the forward's grid of one
  * workgroup per 128 query rows and head; with a selection, the forward may
- * cut its last round of workgroups in two, which this kernel does not; "Out of the Memory
+ * cut its last pass of workgroups in two, which this kernel does not; "Out of the Memory
  * Barrier", gist.science de, section 2.B: attention reads K/V page by page
  * through the table) and computes nothing.  out: caller-owned device buffer
  * of ceil(n_q / 128) * n_q_heads floats (one word per workgroup, contents

@@ -30,7 +30,7 @@ struct __align__(1024) DkvSmem {
 // workgroups dealt out last are the short ones.  An item is two int4: (g,
 // 128-key slab, first iteration, end iteration) and (page-table slot of the
 // slab's page, number of query pages, mask words 0 and 1), so that a
-// workgroup has everything it needs after one round of loads when the chunk
+// workgroup has everything it needs after one set of loads when the chunk
 // has at most 64 query pages.  Every phase runs over all entries at once: no
 // step is sequential over the query pages.
 __global__ void __launch_bounds__(1024) dkdv_plan_kernel(SelDev sel, int hkv, int G, int page,

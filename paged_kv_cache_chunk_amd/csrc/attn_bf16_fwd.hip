@@ -288,9 +288,9 @@ __global__ void __launch_bounds__(256) fwd_merge_kernel(AttnCall c, int n_qblock
 
 TailSplit plan_tail_split(int units, int slots) {
   TailSplit sp;
-  if (slots <= 0 || units < slots) return sp;  // a single round (or less)
+  if (slots <= 0 || units < slots) return sp;  // a single pass (or less)
   const int r = units % slots;
-  // no split when the last round is full or nearly so
+  // no split when the last pass is full or nearly so
   if (r == 0 || 10 * r > 9 * slots) return sp;
   sp.n_whole = units - r;
   sp.n_split = r;

@@ -392,7 +392,7 @@ pkv_status pkv_attn_fwd(pkv_pool* pool, int32_t layer, int64_t q_pos0, int64_t n
   c.o_out = o;
   c.lse = lse;
   if (sel && pool->desc.kv_dtype == PKV_BF16) {
-    // top-K: every unit attends about as many keys; split the last round
+    // top-K: every unit attends about as many keys; split the last pass
     const int slots = 2 * pool->n_cus;
     TailSplit sp = plan_tail_split((int)cdiv(n_q, kFwdRows) * n_q_heads, slots);
     if (sp.n_split > 0) {

@@ -56,8 +56,8 @@ struct DkvPlan {
 // Tail split of a bf16 forward launch whose work units (128 query rows of one
 // head) all cost about the same, as in top-K mode, where every query page
 // attends the same number of pages.  The kernel fits two workgroups on a CU,
-// so U units on S = 2 x CUs slots take ceil(U / S) rounds of work although
-// they hold U / S: with U = q S + r, the last round leaves S - r slots idle.
+// so U units on S = 2 x CUs slots take ceil(U / S) passes of work although
+// they hold U / S: with U = q S + r, the last pass leaves S - r slots idle.
 // The last r units are therefore cut in two along their key tiles, a first
 // part with the fraction cut_num / cut_den of the tiles (r / S, or 1/2 when
 // r < S / 2) and a second part with the rest.  Dispatched after the q S whole

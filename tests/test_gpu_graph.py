@@ -31,7 +31,7 @@ CASES = {
                                       top_k=4), 4),
     "f32_topk": (lambda: get_config("tiny_f32"), 2),
     # a last chunk of 28 query blocks x 28 heads: on a 256-CU device the
-    # forward splits its last round of workgroups and adds a merge kernel
+    # forward splits its last pass of workgroups and adds a merge kernel
     "bf16_topk_split": (lambda: mini_config("qwen_256k_topk", n_ctx=2 * 3584, chunk=3584,
                                             top_k=6), 6),
 }

@@ -223,9 +223,9 @@ def _split_plan(units: int):
     (2816, 2816, 3, 256),  # pages of 256 (4 key tiles each, a part may start inside a page): 616 units, 104 split
 ])
 def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k, page):
-    """Top-K chunks large enough that the bf16 forward cuts its last round of
+    """Top-K chunks large enough that the bf16 forward cuts its last pass of
     work units in two parts along their key tiles (every unit attends about
-    as many keys, so a partial last round would leave slots idle): each part
+    as many keys, so a partial last pass would leave slots idle): each part
     keeps a partial softmax state and a second kernel combines the two.  O,
     LSE, dQ, dK, dV against the oracle, every element; and a second run
     bit-identical."""
@@ -234,7 +234,7 @@ def test_bf16_topk_forward_tail_split(n_ctx, chunk, top_k, page):
     plans = [_split_plan(-(-cfg.chunk_range(c)[1] // 128) * cfg.hq) for c in range(cfg.n_chunks)]
     print(f"splits per chunk: {plans}", flush=True)
     if not any(n for n, _ in plans):
-        pytest.skip("no chunk of this case has a split last round on this device")
+        pytest.skip("no chunk of this case has a split last pass on this device")
     sp = Sparse(top_k=top_k)
     w = Workload(cfg)
     got = run_layer(cfg, w, sparse=sp)
