@@ -33,8 +33,11 @@ COMMON = [
 # measurement on MI355X: the dK/dV and forward kernels (one or two waves per
 # SIMD, register-bound) gain from the iterative ILP scheduler, which hoists LDS
 # reads ahead of the MFMAs that consume them; the dQ kernel from the max-ILP one.
+# dK/dV also takes MFMA results in VGPRs (its K/V operands are pinned to
+# AGPRs in the source), so the softmax reads S and dP without AGPR copies.
 SOURCE_FLAGS = {
-    "attn_bf16_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bf16_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
+                           "-mllvm", "-amdgpu-mfma-vgpr-form"],
     "attn_bf16_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "attn_bf16_dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }

@@ -264,6 +264,13 @@ dkdv_bf16_kernel(AttnCall c, int splits) {
 
   issue(0, it0);
   wait_dma_and_sync();
+  // K and V stay in accumulation registers (AGPRs; MFMA reads its A/B
+  // operands from there), so that the S/dP and dV/dK accumulators, built
+  // with -amdgpu-mfma-vgpr-form, take the VGPRs and the softmax reads S and
+  // dP without 64 v_accvgpr_read per tile.  Placed after the first wait, so
+  // the K/V loads overlap the first tile's copy.
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
   for (int it = it0; it < it1; ++it) {
     const int b = (it - it0) & 1;
     if (it + 1 < it1) issue(b ^ 1, it + 1);
