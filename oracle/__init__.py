@@ -32,7 +32,7 @@ invariants).  No function here is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     depage, page_in, attn_fwd, attn_bwd, run_chunks, rows_fwd_bwd,
-    key_grads_sampled, allowed_pages_matrix,
+    key_grads_sampled, chunk_page_grads, allowed_pages_matrix,
 )
 from .select import key_page_means, query_page_means, select_pages  # noqa: F401
 from .brute import attn_brute  # noqa: F401

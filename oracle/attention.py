@@ -242,3 +242,49 @@ def key_grads_sampled(s0: int, q_all, do_all, k, v, scale: float, chunk: int,
             dk[:nk - s0, g] += scale * (res["dS"][:, s0:].T @ q_all[r0:r1, h].astype(np.float64))
             dv[:nk - s0, g] += res["P"][:, s0:].T @ do_all[r0:r1, h].astype(np.float64)
     return dk, dv
+
+
+def chunk_page_grads(q, do, q_pos0: int, k, v, scale: float, page: int, sel, pages):
+    """dK, dV that one top-K chunk adds to the key pages listed in `pages`.
+
+    Attention restricted to the selected pages (gist.science de, section 2.D;
+    nl "Methodologie"): a row t of query page i and head h attends to the keys
+    s <= t of the pages sel[i][g(h)].  Only those keys enter its softmax, so
+    each (query page, head) is computed against the keys of its selection,
+    gathered in page order (the same softmax as the masked form over all
+    keys; the columns it masks out are simply not formed).  From each row's
+    P and dS the columns of the listed pages give their contributions
+    dK += tau dS^T q and dV += P^T dO.  The work is rows x selected keys,
+    which makes the shared pages of a full-size chunk checkable.
+    q, do [n_q][hq][d]; k, v logical [>= q_pos0 + n_q][hkv][d]; sel[i][g]
+    page ids.  Returns dk, dv [len(pages)][page][hkv][d] (rows past the end
+    of the keys stay zero)."""
+    n_q, hq, d = q.shape
+    hkv = k.shape[1]
+    G = hq // hkv
+    n_keys = q_pos0 + n_q
+    want = {int(p): j for j, p in enumerate(pages)}
+    dk = np.zeros((len(pages), page, hkv, d))
+    dv = np.zeros((len(pages), page, hkv, d))
+    for il in range(-(-n_q // page)):
+        r0, r1 = il * page, min(n_q, (il + 1) * page)
+        t_abs = q_pos0 + np.arange(r0, r1)
+        for g in range(hkv):
+            sel_pages = sorted(int(x) for x in sel[il][g])
+            pos = np.concatenate([np.arange(p * page, min((p + 1) * page, n_keys))
+                                  for p in sel_pages])
+            kk = k[pos, g].astype(np.float64)
+            vv = v[pos, g].astype(np.float64)
+            mask = pos[None, :] <= t_abs[:, None]
+            for h in range(g * G, (g + 1) * G):
+                qh = q[r0:r1, h].astype(np.float64)
+                doh = do[r0:r1, h].astype(np.float64)
+                res = _rows(qh, kk, vv, doh, t_abs, scale, mask)
+                for p in sel_pages:
+                    if p not in want:
+                        continue
+                    cols = np.nonzero(pos // page == p)[0]
+                    n = len(cols)
+                    dk[want[p], :n, g] += scale * (res["dS"][:, cols].T @ qh)
+                    dv[want[p], :n, g] += res["P"][:, cols].T @ doh
+    return dk, dv

@@ -5,6 +5,9 @@ append), on outputs the oracle can compute one by one:
     three query heads);
   * dK, dV of the last keys of the context in full (only the last rows see
     them, so the oracle's cost stays small);
+  * at 256K top-K, the last chunk's own dK/dV contribution (the sweep's first
+    backward) to the sink page and the three pages its query pages share
+    most, every element;
   * for every key, the sums that hold at any size: sum_s dK = 0 and
     sum_s dV = sum of dO over the group's heads and all rows;
   * in top-K mode, the selections (exact, up to the 1e-5 score-gap rule;
@@ -27,7 +30,7 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _run(cfg, sample_rows, sample_heads, sel_chunks=()):
+def _run(cfg, sample_rows, sample_heads, sel_chunks=(), shared_pages=0):
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, Sparse
@@ -43,6 +46,7 @@ def _run(cfg, sample_rows, sample_heads, sel_chunks=()):
     for ch in chunks:
         pkv.pkv_append_kv(pool, 0, ch["q_pos0"], ch["k"], ch["v"])
     samples, sels = {}, {}
+    first_pages = None
     for c in reversed(range(len(chunks))):
         ch = chunks[c]
         n = ch["q"].shape[0]
@@ -60,6 +64,27 @@ def _run(cfg, sample_rows, sample_heads, sel_chunks=()):
                           lse=b.lse[:, ri].cpu().numpy(), dq=b.dq[ri].cpu().numpy())
         if sparse is not None and c in sel_chunks:
             sels[c] = (b.sel[0].cpu().numpy(), b.sel[1].cpu().numpy())
+        if shared_pages and c == len(chunks) - 1:
+            # the first backward of the sweep: the pool's dK/dV hold this
+            # chunk's contribution only.  Keep the sink page and the pages
+            # the chunk's query pages share most (many work items, one atomic
+            # epilogue each).
+            pg, cnt = b.sel[0].cpu().numpy(), b.sel[1].cpu().numpy()
+            hits = np.zeros(cfg.n_pages, dtype=np.int64)
+            for il in range(pg.shape[0]):
+                for g in range(cfg.hkv):
+                    hits[pg[il, g, :cnt[il, g]]] += 1
+            hits[0] = -1
+            shared = [0] + [int(x) for x in np.argsort(-hits, kind="stable")[:shared_pages - 1]]
+            first = dict(pages=shared, lists=[int(cnt.size) if p == 0 else int(hits[p])
+                                              for p in shared], dk=[], dv=[])
+            for p in shared:
+                for what, key in ((pkv.PKV_DK, "dk"), (pkv.PKV_DV, "dv")):
+                    dst = torch.empty(cfg.page, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+                    pkv.pkv_read_rows(pool, 0, what, p * cfg.page, dst)
+                    torch.cuda.synchronize()
+                    first[key].append(dst.cpu().numpy())
+            first_pages = first
     N = cfg.n_ctx
     dk = torch.empty(N, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)
@@ -72,7 +97,7 @@ def _run(cfg, sample_rows, sample_heads, sel_chunks=()):
                   for ch in chunks).cpu().numpy() for g in range(cfg.hkv)]
     pool.close()
     return dict(chunks=chunks, samples=samples, sels=sels, dk=dk.cpu().numpy(),
-                dv=dv.cpu().numpy(), do_sum=do_sum, **host)
+                dv=dv.cpu().numpy(), do_sum=do_sum, first_pages=first_pages, **host)
 
 
 def _oracle_sel(cfg, got, c):
@@ -129,6 +154,18 @@ def _check(cfg, got, heads, key_tail, sel_chunks=()):
                                       cfg.chunk, cfg.page, sels)
     worst["dk_tail"] = rel_err(got["dk"][s0:], dk)
     worst["dv_tail"] = rel_err(got["dv"][s0:], dv)
+    first = got.get("first_pages")
+    if first is not None:
+        # the last chunk's own contribution to the sink and the most shared
+        # pages, every element, against the oracle on the same selection
+        pages = first["pages"]
+        rdk, rdv = oracle.chunk_page_grads(last["q"].float().cpu().numpy(),
+                                           last["do"].float().cpu().numpy(), last["q_pos0"], k, v,
+                                           cfg.scale, cfg.page, osel[cfg.n_chunks - 1], pages)
+        worst["dk_shared_pages"] = rel_err(np.stack(first["dk"]), rdk)
+        worst["dv_shared_pages"] = rel_err(np.stack(first["dv"]), rdv)
+        print(f"{cfg.name}: last chunk's dK/dV of pages {pages} (held by {first['lists']} of the "
+              f"chunk's (query page, KV head) lists) checked element-wise", flush=True)
     # sums over every key
     for g in range(cfg.hkv):
         sk = np.abs(got["dk"][:, g].astype(np.float64).sum(0)).max()
@@ -157,7 +194,7 @@ def test_qwen_256k_topk_full():
     scoring; sampled rows of every chunk on the oracle's selection."""
     cfg = get_config("qwen_256k_topk")
     every = tuple(range(cfg.n_chunks))
-    got = _run(cfg, lambda n: [128, 2049], None, sel_chunks=every)
+    got = _run(cfg, lambda n: [128, 2049], None, sel_chunks=every, shared_pages=4)
     _check(cfg, got, heads=(0, 15), key_tail=32, sel_chunks=every)
 
 

@@ -273,6 +273,42 @@ def test_sampled_helpers_match_full(sparse):
     assert _rel(dv, r["dv"][s0:]) < 1e-13
 
 
+def test_chunk_page_grads_against_brute_force_and_masked_form():
+    """One top-K chunk's contribution to chosen key pages (keys gathered per
+    selection) equals the per-(t, h, s) loops of the brute-force oracle run on
+    that chunk alone, and the masked full-key form."""
+    q, k, v, do = _micro(23, N=48, hq=4, hkv=2, d=8)
+    chunk, page, scale = 16, 4, 0.3
+    sp = dict(top_k=2, n_sink=1, n_local=2)
+    r = oracle.run_chunks(q, k, v, do, chunk, scale, page, sparse=sp)
+    c = 2                              # last chunk: rows 32..47, keys 0..47
+    q_pos0 = c * chunk
+    sel = r["sel"][c]
+    pages = [0, 3, 5, 11]             # sink, earlier pages, the last query page
+    dk, dv = oracle.chunk_page_grads(q[q_pos0:], do[q_pos0:], q_pos0, k, v, scale, page, sel,
+                                     pages)
+    n = q_pos0 + chunk
+    # brute force (per-(t, h, s) loops) over the chunks up to this one, with
+    # dO = 0 on the rows of earlier chunks: they then add nothing to dK/dV,
+    # which leaves this chunk's contribution
+    doz = np.zeros_like(do[:n])
+    doz[q_pos0:] = do[q_pos0:n]
+    sels_b = [[[list(map(int, s_)) for s_ in row] for row in r["sel"][cc]] for cc in range(c + 1)]
+    b = attn_brute(q[:n].tolist(), k[:n].tolist(), v[:n].tolist(), doz.tolist(), chunk, scale,
+                   page, sels_b)
+    bk, bv = np.array(b[3]), np.array(b[4])
+    for j, p_ in enumerate(pages):
+        sl = slice(p_ * page, (p_ + 1) * page)
+        assert np.abs(dk[j] - bk[sl]).max() < 1e-13 and np.abs(dv[j] - bv[sl]).max() < 1e-13
+    # the masked form of one chunk (attn_bwd over all keys up to the chunk)
+    m = oracle.attn_bwd(q[q_pos0:n], k, v, do[q_pos0:n], q_pos0, scale, page, sel)
+    for j, p_ in enumerate(pages):
+        sl = slice(p_ * page, (p_ + 1) * page)
+        assert _rel(dk[j], m["dk"][sl]) < 1e-13 and _rel(dv[j], m["dv"][sl]) < 1e-13
+    # the sink page is held by every query page, so it did receive gradient
+    assert np.abs(dv[0]).max() > 0
+
+
 def test_page_in_depage_roundtrip_and_pool_bytes():
     cfg = get_config("tiny_f32")
     w = Workload(cfg)
