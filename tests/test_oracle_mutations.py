@@ -37,6 +37,9 @@ PINS = {
     "sum_identities_sparse": lambda: P.test_gradient_sum_identities(dict(top_k=2)),
     "closed_forms": P.test_closed_forms,
     "hand_worked": P.test_hand_worked_two_tokens,
+    "sampled_helpers": lambda: P.test_sampled_helpers_match_full(None),
+    "sampled_helpers_sparse": lambda: P.test_sampled_helpers_match_full(dict(top_k=2)),
+    "chunk_page_grads": P.test_chunk_page_grads_against_brute_force_and_masked_form,
 }
 
 # (module, function, exact source text, replacement)
@@ -79,6 +82,16 @@ MUTANTS = {
                       "forced = set() | "),
     "one_page_too_many": (OS, "select_pages", "keep = cand[order[:min(top_k, cand.size)]]",
                           "keep = cand[order[:min(top_k + 1, cand.size)]]"),
+    "page_grads_dk_without_scale": (OA, "chunk_page_grads", 'dk[want[p], :n, g] += scale * (res["dS"]',
+                                    'dk[want[p], :n, g] += (res["dS"]'),
+    "page_grads_strict_causal": (OA, "chunk_page_grads", "mask = pos[None, :] <= t_abs[:, None]",
+                                 "mask = pos[None, :] < t_abs[:, None]"),
+    "page_grads_next_page_columns": (OA, "chunk_page_grads", "cols = np.nonzero(pos // page == p)[0]",
+                                     "cols = np.nonzero(pos // page == min(p + 1, sel_pages[-1]))[0]"),
+    "page_grads_dv_from_q": (OA, "chunk_page_grads", 'dv[want[p], :n, g] += res["P"][:, cols].T @ doh',
+                             'dv[want[p], :n, g] += res["P"][:, cols].T @ qh'),
+    "page_grads_group_mapping": (OA, "chunk_page_grads", "for h in range(g * G, (g + 1) * G):",
+                                 "for h in range(g, hq, hkv):"),
 }
 
 
