@@ -318,7 +318,12 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
  * pkv_writeback_grads) returns PKV_ESTATE.  With a window smaller than a
  * layer, the pages a selection can name per KV head, min(n_qpages x stride,
  * pages appended), must fit window_slots, else PKV_ECAPACITY and nothing
- * is enqueued. */
+ * is enqueued.  A prefetch that fails after those checks (a HIP call
+ * failing: PKV_EHIP) leaves the window holding no layer: attention on the
+ * window's layers returns PKV_ESTATE until a prefetch succeeds, and the
+ * prefetch can simply be called again.  (Test hook: PKV_FAIL_COPY_AT=n in
+ * the environment makes the n-th host-link copy of a pool, a prefetch's
+ * fetch or a writeback, fail this way before it is enqueued.) */
 pkv_status pkv_prefetch_pages(pkv_pool* pool, int32_t layer, const pkv_sel* sel,
                               int32_t with_grads, hipStream_t copy_stream, hipEvent_t ready);
 
@@ -349,7 +354,9 @@ pkv_status pkv_prefetch_prefix(pkv_pool* pool, int32_t layer, int64_t n_keys, in
  * them into the host tier; the call first waits (on the host) until the adds
  * of the window's previous writeback have finished, since they read the
  * same staging, and a second writeback of one prefetch is PKV_ESTATE (it
- * would add the same contributions twice). */
+ * would add the same contributions twice).  A writeback whose copies fail
+ * to enqueue (PKV_EHIP) leaves the window's gradients in place, and calling
+ * it again writes them back. */
 pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_stream,
                                hipEvent_t done);
 

@@ -28,6 +28,16 @@ bool injected_failure(pkv_pool* p) {
   return ++p->allocs == std::atoi(now);
 }
 
+// Test hook: PKV_FAIL_COPY_AT=n makes the n-th host-link copy of a pool (the
+// fetch of a prefetch, or a writeback) fail as if its launch had failed,
+// before anything of it is enqueued, so that tests can check the pool's state
+// after a failed transfer.
+bool injected_copy_failure(pkv_pool* p) {
+  const char* now = std::getenv("PKV_FAIL_COPY_AT");
+  if (!now) return false;
+  return ++p->copies == std::atoi(now);
+}
+
 pkv_status dev_alloc(pkv_pool* p, void** ptr, int64_t bytes, const char* what) {
   *ptr = nullptr;
   if (bytes <= 0) return PKV_OK;
@@ -394,6 +404,15 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
              (long long)bound, p->window_slots);
     return pool_fail(PKV_ECAPACITY, msg);
   }
+  // From here on the window's old content is given up (its table is
+  // rewritten below): until this prefetch has been enqueued completely, no
+  // layer is in the window, so that a prefetch that fails part-way leaves
+  // attention on the window rejected (PKV_ESTATE) rather than reading pages
+  // that were never fetched.
+  p->window_layer[w] = -1;
+  p->window_grads[w] = false;
+  p->window_keys[w] = 0;
+  p->zero_pending[w] = false;
   // K/V of the window are free once the attention calls on its last layer ran
   if (p->compute_recorded[w]) {
     if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
@@ -419,9 +438,6 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
         (e = hipEventRecord(p->ev_count[w], cs)) != hipSuccess)
       return pool_hip_fail(e, "pkv_prefetch_pages: list length");
   }
-  p->window_layer[w] = layer;
-  p->window_grads[w] = with_grads;
-  p->window_keys[w] = n_avail;
   // Gradients fetched into HBM (no host accumulation): one launch for K/V and
   // gradients after the window's last writeback has read its gradients.
   // Fetching K/V before that wait and the gradients after it ran the K/V
@@ -432,8 +448,13 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
     if ((e = hipStreamWaitEvent(cs, p->ev_wb[w], 0)) != hipSuccess)
       return pool_hip_fail(e, "hipStreamWaitEvent (window writeback)");
   }
+  if (injected_copy_failure(p)) return pool_hip_fail(hipErrorLaunchFailure,
+                                                    "pkv_prefetch_pages: fetch (injected, PKV_FAIL_COPY_AT)");
   if ((e = launch_fetch(p, layer, w, cs, grads_now)) != hipSuccess)
     return pool_hip_fail(e, "pkv_prefetch_pages: fetch");
+  p->window_layer[w] = layer;
+  p->window_grads[w] = with_grads;
+  p->window_keys[w] = n_avail;
   p->zero_pending[w] = with_grads && p->accumulate;
   if ((e = hipEventRecord(p->ev_ready[w], cs)) != hipSuccess)
     return pool_hip_fail(e, "hipEventRecord (window ready)");
@@ -466,6 +487,8 @@ pkv_status pool_writeback(pkv_pool* p, int layer, hipStream_t cs, hipEvent_t don
     if ((e = p->adder->wait(p->stage_ticket[w])) != hipSuccess)
       return pool_hip_fail(e, "host gradient adds: hipEventSynchronize");
   }
+  if (injected_copy_failure(p)) return pool_hip_fail(hipErrorLaunchFailure,
+                                                    "pkv_writeback_grads: (injected, PKV_FAIL_COPY_AT)");
   const pkv_pool_desc& d = p->desc;
   const int64_t need_w = need_words(p);
   const int b = p->list_gen[w];

@@ -49,6 +49,7 @@ struct pkv_pool {
   int64_t device_bytes = 0;
   int64_t host_bytes = 0;
   int allocs = 0;  // allocations made so far by pool creation (failure-injection hook)
+  int copies = 0;  // host-link copies enqueued so far (failure-injection hook)
 
   // Host tier (pinned, device-mapped), per layer.
   static constexpr int kWindow = 2;

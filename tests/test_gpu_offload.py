@@ -283,6 +283,81 @@ def test_host_accumulate_state_errors():
     pool.close()
 
 
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_failed_transfers_leave_a_consistent_pool(accumulate):
+    """A prefetch or a writeback whose copy fails to enqueue (forced through
+    the library's test hook PKV_FAIL_COPY_AT=n: the n-th host-link copy of
+    the pool, counted while the variable is set, fails as a failed launch
+    would) returns PKV_EHIP.  After the failed prefetch the window holds no
+    layer, so attention on it is PKV_ESTATE instead of reading pages that
+    were never fetched; after the failed writeback the window's gradients
+    stay in place.  Retrying both gives what a run without failures gives:
+    O, LSE and dQ bit-identical, dK/dV within fp32 summation-order noise
+    (fp32 host gradients)."""
+    import os
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    cfg = CFG.replace(n_layers=2)
+    w = Workload(cfg, layer=1)
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    last = w.chunk(cfg.n_chunks - 1)
+    n_keys = last.q_pos0 + last.n_q
+
+    def run(fail):
+        pool = pkv.pkv_pool_create(2, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
+                                   pkv.PKV_BF16, host_tier=1, host_grad_dtype=pkv.PKV_F32,
+                                   host_grad_accumulate=accumulate)
+        tab = w.table()
+        for g in range(cfg.hkv):
+            pkv.pkv_page_table_set(pool, 1, g, tab[g])
+        for c in range(cfg.n_chunks):
+            ch = w.chunk(c)
+            pkv.pkv_append_kv(pool, 1, ch.q_pos0, dev(ch.k), dev(ch.v))
+        q, do = dev(last.q), dev(last.do)
+        o = torch.empty_like(q)
+        lse = torch.empty(cfg.hq, last.n_q, device="cuda")
+        dq = torch.empty(last.n_q, cfg.hq, cfg.d, device="cuda")
+        if fail:
+            os.environ["PKV_FAIL_COPY_AT"] = "1"      # the pool's first copy: this fetch
+            try:
+                with pytest.raises(pkv.PkvError) as e:
+                    pkv.pkv_prefetch_prefix(pool, 1, n_keys, with_grads=True)
+            finally:
+                del os.environ["PKV_FAIL_COPY_AT"]
+            assert e.value.status == 5 and "injected" in str(e.value), str(e.value)
+            with pytest.raises(pkv.PkvError) as e:
+                pkv.pkv_attn_fwd(pool, 1, last.q_pos0, q, o, lse, cfg.scale)
+            assert e.value.status == 4  # PKV_ESTATE: the window holds no layer
+        pkv.pkv_prefetch_prefix(pool, 1, n_keys, with_grads=True)
+        pkv.pkv_attn_fwd(pool, 1, last.q_pos0, q, o, lse, cfg.scale)
+        pkv.pkv_attn_bwd(pool, 1, last.q_pos0, q, o, do, lse, dq, cfg.scale)
+        if fail:
+            os.environ["PKV_FAIL_COPY_AT"] = "2"      # the next copy counted: this writeback
+            try:
+                with pytest.raises(pkv.PkvError) as e:
+                    pkv.pkv_writeback_grads(pool, 1)
+            finally:
+                del os.environ["PKV_FAIL_COPY_AT"]
+            assert e.value.status == 5 and "injected" in str(e.value), str(e.value)
+        pkv.pkv_writeback_grads(pool, 1)
+        dk = torch.empty(cfg.n_ctx, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        pkv.pkv_read_pages(pool, 1, pkv.PKV_DK, dk)
+        pkv.pkv_read_pages(pool, 1, pkv.PKV_DV, dv)
+        torch.cuda.synchronize()
+        out = dict(O=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.cpu().numpy(),
+                   dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
+        pool.close()
+        return out
+
+    ok, failed = run(False), run(True)
+    for name in ("O", "lse", "dq"):
+        assert np.array_equal(failed[name], ok[name]), name
+    for name in ("dk", "dv"):
+        assert np.abs(ok[name]).max() > 0
+        assert rel_err(failed[name], ok[name]) < 1e-5, name
+
+
 # 64 pages per layer, chunks of 4 query pages, top-K 6 + 3 forced: a visit
 # names at most 4 x 9 = 36 pages per KV head, so a window of 36 slots per head
 # holds any selection while a layer has 64 pages
