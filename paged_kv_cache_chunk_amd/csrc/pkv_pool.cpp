@@ -288,7 +288,13 @@ pkv_status pool_append(pkv_pool* p, int layer, int64_t pos0, int64_t n_tok, cons
   // chunk can attend to its own keys without another prefetch.
   if (p->desc.host_tier && p->window_layer[w] == layer && pos0 + n_tok <= p->window_keys[w]) {
     e = launch_append(layer_view(p, layer), compute_geom(p), p->kv_bytes, pos0, n_tok, k, v, s);
-    if (e != hipSuccess) return pool_hip_fail(e, "pkv_append_kv: window append launch");
+    if (e != hipSuccess) {
+      // the window lacks these rows now: it no longer holds the layer
+      p->window_layer[w] = -1;
+      p->window_grads[w] = false;
+      p->window_keys[w] = 0;
+      return pool_hip_fail(e, "pkv_append_kv: window append launch");
+    }
     return pool_after_compute(p, layer, s);  // the next prefetch into the window waits for it
   }
   return PKV_OK;
