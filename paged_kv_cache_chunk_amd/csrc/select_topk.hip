@@ -31,13 +31,15 @@ __device__ __forceinline__ float ld(const void* p, int64_t i, bool bf16) {
 // tid % 32) sums columns j*E .. j*E+E-1 (E = d / 32) over the (token, head)
 // pairs p, p + 32, .. of the page's group in that order; the 32 partial
 // sums are then added in part order.  Fixed order, so reruns are
-// bit-identical.
-template <int DD>
+// bit-identical.  The loads of four pairs are issued before their adds (which
+// keep the pair order), so that their latencies overlap.
+template <int DD, bool BF16>
 __global__ void __launch_bounds__(1024) qmean_kernel(const void* __restrict__ q,
                                                      float* __restrict__ qbar, int hq, int hkv,
-                                                     int page, int n_q, bool bf16) {
+                                                     int page, int n_q) {
   constexpr int E = DD / 32;
   constexpr int NP = 32;
+  constexpr int U = 4;  // pairs loaded ahead of their adds
   __shared__ float red[NP][DD];
   const int il = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int part = tid >> 5, j = tid & 31;
@@ -46,29 +48,45 @@ __global__ void __launch_bounds__(1024) qmean_kernel(const void* __restrict__ q,
   int t1 = t0 + page;
   if (t1 > n_q) t1 = n_q;
   const int n_pairs = (t1 - t0) * G;
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int pr = part; pr < n_pairs; pr += NP) {
+  // this thread's E values of pair pr, widened to fp32
+  auto load = [&](int pr, float (&x)[E]) {
     const int t = t0 + pr / G, h = g * G + pr % G;
     const int64_t base = ((int64_t)t * hq + h) * DD + j * E;
-    if (bf16) {
+    if (BF16) {
       // E consecutive bf16 values (4 or 2): one 8- or 4-byte load
       const unsigned short* p = reinterpret_cast<const unsigned short*>(q) + base;
       if (E == 4) {
         const uint2 v = *reinterpret_cast<const uint2*>(p);
-        acc[0] += __uint_as_float(v.x << 16);
-        acc[1] += __uint_as_float(v.x & 0xffff0000u);
-        acc[E > 2 ? 2 : 0] += E > 2 ? __uint_as_float(v.y << 16) : 0.f;
-        acc[E > 3 ? 3 : 0] += E > 3 ? __uint_as_float(v.y & 0xffff0000u) : 0.f;
+        const unsigned w[4] = {v.x << 16, v.x & 0xffff0000u, v.y << 16, v.y & 0xffff0000u};
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = __uint_as_float(w[e]);
       } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += __uint_as_float(((unsigned)p[e]) << 16);
+        for (int e = 0; e < E; ++e) x[e] = __uint_as_float(((unsigned)p[e]) << 16);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += reinterpret_cast<const float*>(q)[base + e];
+      for (int e = 0; e < E; ++e) x[e] = reinterpret_cast<const float*>(q)[base + e];
     }
+  };
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  int pr = part;
+  for (; pr + (U - 1) * NP < n_pairs; pr += U * NP) {
+    float x[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load(pr + u * NP, x[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += x[u][e];
+  }
+  for (; pr < n_pairs; pr += NP) {
+    float x[E];
+    load(pr, x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += x[e];
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) red[part][j * E + e] = acc[e];
@@ -261,12 +279,15 @@ hipError_t launch_select(const LayerDev& L, const Geom& g, bool bf16, int hq, in
   KernelTimer t(KT_SELECT, s);
   float* qbar = scratch;
   float* scores = scratch + (int64_t)nqp * g.hkv * g.d;
-  if (g.d == 64)
-    hipLaunchKernelGGL(qmean_kernel<64>, dim3(nqp, g.hkv), dim3(1024), 0, s, q, qbar, hq, g.hkv,
-                       g.page, n_q, bf16);
+  const dim3 qgrid(nqp, g.hkv);
+  if (g.d == 64 && bf16)
+    hipLaunchKernelGGL((qmean_kernel<64, true>), qgrid, dim3(1024), 0, s, q, qbar, hq, g.hkv, g.page, n_q);
+  else if (g.d == 64)
+    hipLaunchKernelGGL((qmean_kernel<64, false>), qgrid, dim3(1024), 0, s, q, qbar, hq, g.hkv, g.page, n_q);
+  else if (bf16)
+    hipLaunchKernelGGL((qmean_kernel<128, true>), qgrid, dim3(1024), 0, s, q, qbar, hq, g.hkv, g.page, n_q);
   else
-    hipLaunchKernelGGL(qmean_kernel<128>, dim3(nqp, g.hkv), dim3(1024), 0, s, q, qbar, hq, g.hkv,
-                       g.page, n_q, bf16);
+    hipLaunchKernelGGL((qmean_kernel<128, false>), qgrid, dim3(1024), 0, s, q, qbar, hq, g.hkv, g.page, n_q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(score_kernel, dim3(nqp, g.hkv, (max_cand + 255) / 256), dim3(256), 0, s,
