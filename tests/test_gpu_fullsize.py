@@ -292,3 +292,105 @@ def test_qwen_1m_offload_last_chunk(accumulate):
           flush=True)
     for name, e in worst.items():
         assert e <= 1e-2, f"{name}: {e:.3e}"
+
+
+def test_four_million_token_layer_last_chunk():
+    """One layer of the top-K workload at a 4,194,304-token context (32768
+    pages per KV head) in the host tier, with windows of 64 x 131 = 8384 slots
+    per KV head (what a chunk of 8192 tokens with top-K 128 + 3 forced pages
+    can name): the pool's HBM stays under the 16 GiB cap, and the backward
+    sweep of the last chunk (selection, prefetch of the selected pages and
+    their gradients, forward, backward, gradient writeback) matches the
+    oracle: the selection of all 64 x 4 lists (1e-5 score-gap rule), O, LSE
+    and dQ of sampled rows, and the chunk's dK/dV contributions to the sink
+    page and the three pages its query pages share most, every element, after
+    their round trip through the bf16 host tier."""
+    import time
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
+    from synthetic.gpu import GpuWorkload
+
+    cfg = get_config("qwen_1m_offload").replace(n_ctx=4 << 20, slots=32768, n_layers=1)
+    assert cfg.n_pages == 32768 and cfg.n_chunks == 512
+    ws = 64 * 131
+    w = GpuWorkload(cfg, layer=0)
+    pool = pkv.pkv_pool_create(1, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots, pkv.PKV_BF16,
+                               host_tier=1, host_grad_dtype=pkv.PKV_BF16, window_slots=ws,
+                               device_budget_bytes=cfg.hbm_cap_bytes)
+    dev_bytes, host_bytes = pkv.pkv_pool_bytes(pool)
+    print(f"4M-token layer: pool HBM {dev_bytes / 2**30:.2f} GiB, pinned {host_bytes / 2**30:.2f} GiB",
+          flush=True)
+    assert dev_bytes < cfg.hbm_cap_bytes
+    tab = w.table()
+    for g in range(cfg.hkv):
+        pkv.pkv_page_table_set(pool, 0, g, tab[g])
+    k = np.empty((cfg.n_ctx, cfg.hkv, cfg.d), dtype=np.float32)
+    v = np.empty_like(k)
+    for c in range(cfg.n_chunks):
+        kv = w.chunk(c, "kv")
+        pkv.pkv_append_kv(pool, 0, kv["q_pos0"], kv["k"], kv["v"])
+        lo = kv["q_pos0"]
+        k[lo:lo + kv["k"].shape[0]] = kv["k"].float().cpu().numpy()
+        v[lo:lo + kv["v"].shape[0]] = kv["v"].float().cpu().numpy()
+    c_last = cfg.n_chunks - 1
+    ch = w.chunk(c_last, "qd")
+    n, q_pos0 = ch["q"].shape[0], ch["q_pos0"]
+    sp = Sparse(cfg.top_k, cfg.n_sink, cfg.n_local)
+    sweep = OffloadSweep(pool, 1, cfg.hq, cfg.hkv, cfg.d, cfg.page, cfg.scale, sp, torch.bfloat16)
+    bufs = {0: ChunkBuffers(n, cfg.hq, cfg.hkv, cfg.d, cfg.page, torch.bfloat16, sp)}
+    rows = sorted({0, 1, 127, 128, n // 2, n - 1})
+    got = {}
+
+    def outputs(l, c, b):
+        ri = torch.tensor(rows, device="cuda")
+        got.update(O=b.o[ri].float().cpu().numpy(), lse=b.lse[:, ri].cpu().numpy(),
+                   dq=b.dq[ri].cpu().numpy(), sel=(b.sel[0].cpu().numpy(), b.sel[1].cpu().numpy()))
+
+    torch.cuda.synchronize()
+    t0 = time.time()
+    sweep.chunk(c_last, lambda l, c: ch, bufs, outputs)
+    torch.cuda.synchronize()
+    print(f"4M-token layer: last chunk's sweep {1e3 * (time.time() - t0):.1f} ms "
+          f"(selection, prefetch, forward, backward, writeback; outputs copied to the host)",
+          flush=True)
+    pg, cnt = got["sel"]
+    hits = np.zeros(cfg.n_pages, dtype=np.int64)
+    for il in range(pg.shape[0]):
+        for g in range(cfg.hkv):
+            hits[pg[il, g, :cnt[il, g]]] += 1
+    hits[0] = -1
+    pages = [0] + [int(x) for x in np.argsort(-hits, kind="stable")[:3]]
+    dk_all = torch.empty(cfg.n_ctx, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+    pkv.pkv_read_pages(pool, 0, pkv.PKV_DK, dk_all)
+    dk = np.stack([dk_all[p * cfg.page:(p + 1) * cfg.page].cpu().numpy() for p in pages])
+    pkv.pkv_read_pages(pool, 0, pkv.PKV_DV, dk_all)
+    dv = np.stack([dk_all[p * cfg.page:(p + 1) * cfg.page].cpu().numpy() for p in pages])
+    del dk_all
+    pool.close()
+    q = ch["q"].float().cpu().numpy()
+    do = ch["do"].float().cpu().numpy()
+    ref_sel, scores = oracle.select_pages(q, k, q_pos0, cfg.page, cfg.hkv, cfg.top_k, cfg.n_sink,
+                                          cfg.n_local, score_dtype=np.float32, return_scores=True)
+    gpu_sel = sel_lists(got["sel"])
+    nd = compare_selection(gpu_sel, ref_sel, scores, cfg.top_k)
+    sel = [[np.array(lst, dtype=np.int64) for lst in row] for row in gpu_sel]
+    worst = {"O": 0.0, "lse": 0.0, "dq": 0.0}
+    t_abs = q_pos0 + np.array(rows)
+    for h in (0, 15, 27):
+        ok = np.zeros((len(rows), cfg.n_pages), dtype=bool)
+        for i, r in enumerate(rows):
+            ok[i, sel[r // cfg.page][h // cfg.group]] = True
+        O, lse, dq = oracle.rows_fwd_bwd(q[rows, h], do[rows, h], t_abs, h, k, v, cfg.scale,
+                                         cfg.group, cfg.page, ok)
+        worst["O"] = max(worst["O"], rel_err(got["O"][:, h], O))
+        worst["lse"] = max(worst["lse"], rel_err(got["lse"][h], lse))
+        worst["dq"] = max(worst["dq"], rel_err(got["dq"][:, h], dq))
+    rdk, rdv = oracle.chunk_page_grads(q, do, q_pos0, k, v, cfg.scale, cfg.page, sel, pages)
+    worst["dk_shared_pages"] = rel_err(dk, rdk)
+    worst["dv_shared_pages"] = rel_err(dv, rdv)
+    print(f"4M-token layer: {nd} lists differ inside the score gap; pages {pages} held by "
+          f"{[int(cnt.size) if p == 0 else int(hits[p]) for p in pages]} lists;",
+          {k_: f"{v_:.2e}" for k_, v_ in worst.items()}, flush=True)
+    for name, e in worst.items():
+        assert e <= 1e-2, f"{name}: {e:.3e}"
