@@ -520,7 +520,7 @@ def traffic_for(kernel: str, workload: str):
 
 
 def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0,
-                  select_ahead: bool = False) -> dict:
+                  select_ahead: bool = False, window_slots: int = 0) -> dict:
     """Host-offloaded stack: every layer's K/V and KV-gradient pools in pinned
     host memory (bf16), an HBM window of two layers, the next layer's
     selected pages prefetched on a side stream during the current layer, and
@@ -532,7 +532,8 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0,
     contributions into the host tier (no gradient bytes host -> HBM).
     select_ahead: the selections are made before the timed backward sweep
     (as the forward sweep makes them) and reused by it; their time is
-    reported apart."""
+    reported apart.  window_slots: page slots per KV head of each HBM window
+    (0: a whole layer)."""
     import torch
     import paged_kv_cache_chunk_amd as pkv
     from paged_kv_cache_chunk_amd.chunks import ChunkBuffers, OffloadSweep, Sparse
@@ -548,7 +549,8 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0,
         pool = pkv.pkv_pool_create(L, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
                                    pkv.PKV_BF16, host_tier=host_tier, host_grad_dtype=pkv.PKV_BF16,
                                    device_budget_bytes=cfg.hbm_cap_bytes if host_tier else 0,
-                                   host_grad_accumulate=host_accumulate if host_tier else 0)
+                                   host_grad_accumulate=host_accumulate if host_tier else 0,
+                                   window_slots=window_slots if host_tier else 0)
         dev_b, host_b = pkv.pkv_pool_bytes(pool)
         for l in range(L):
             tab = ws[l].table()
@@ -641,7 +643,9 @@ def offload_bench(cfg, steps: int, resident_ab: bool, host_accumulate: int = 0,
         "workload": f"{cfg.name}: {L} layers, {cfg.n_ctx} tokens, chunks of {cfg.chunk}, "
                     + (f"top-K {cfg.top_k} + {cfg.n_sink} sink + {cfg.n_local} local pages"
                        if cfg.sparse else "dense causal")
-                    + ", K/V and gradient pools in pinned host memory (bf16), HBM window of 2 layers"
+                    + ", K/V and gradient pools in pinned host memory (bf16), "
+                    + (f"two HBM windows of {window_slots} page slots per KV head" if window_slots
+                       else "HBM window of 2 layers")
                     + (", gradient contributions added on the host" if host_accumulate else
                        ", gradients accumulated in HBM"),
         "host_grad_accumulate": host_accumulate,
@@ -815,6 +819,11 @@ def main():
     ap.add_argument("--select-ahead", action="store_true",
                     help="offloaded top-K workload: make every selection before the timed backward "
                          "sweep (as the forward sweep does) and reuse them")
+    ap.add_argument("--context", type=int, default=0,
+                    help="offloaded workload: context length in tokens (default: the config's)")
+    ap.add_argument("--window-slots", type=int, default=0,
+                    help="offloaded workload: page slots per KV head of each HBM window "
+                         "(default: a whole layer)")
     ap.add_argument("--resident-ab", action="store_true",
                     help="offloaded workload: also run the same sweep with all pools in HBM")
     ap.add_argument("--topk-sweep", default="", metavar="K1,K2,..",
@@ -905,8 +914,10 @@ def main():
     if cfg.host_tier:
         if args.layers:
             cfg = cfg.replace(n_layers=args.layers)
+        if args.context:
+            cfg = cfg.replace(n_ctx=args.context, slots=-(-args.context // cfg.page))
         res = offload_bench(cfg, args.chunks, args.resident_ab, args.host_accumulate,
-                            args.select_ahead)
+                            args.select_ahead, args.window_slots)
         res.update({"metric": f"offloaded {'top-K' if cfg.sparse else 'dense'} stack: "
                               "backward-sweep tokens/s per layer",
                     "unit": "tokens/s", "n_gpus": 1, "dtype": "bf16", "data": "synthetic"})
