@@ -135,3 +135,32 @@ def test_equal_pages_tie_to_the_lower_pages():
             assert sel[0][0].tolist() == [1, 2, 3, n_pages - 1], (seed, d, dtype)
         assert brute_select(q.tolist(), k.tolist(), q_pos0, page, 1, top_k, 0, 1) == \
             [[[1, 2, 3, n_pages - 1]]]
+
+
+@SETTINGS
+@given(shapes(), st.integers(0, 4), st.integers(0, 2), st.integers(1, 3))
+def test_page_grads_match_brute_force(s, top_k, n_sink, n_local):
+    """A top-K chunk's dK/dV contribution to every key page, computed from the
+    keys of each selection alone (oracle.chunk_page_grads), equals the
+    brute-force loops run over the chunks up to it with dO = 0 on the rows of
+    earlier chunks (which then add nothing to dK/dV)."""
+    q, k, v, do, page, chunk, scale = s
+    n = q.shape[0]
+    sp = dict(top_k=top_k, n_sink=n_sink, n_local=n_local)
+    r = oracle.run_chunks(q, k, v, do, chunk, scale, page, sparse=sp)
+    c = (n - 1) // chunk                          # the last chunk
+    q_pos0 = c * chunk
+    sel = r["sel"][c]
+    pages = list(range(-(-n // page)))
+    dk, dv = oracle.chunk_page_grads(q[q_pos0:], do[q_pos0:], q_pos0, k, v, scale, page, sel,
+                                     pages)
+    doz = np.zeros_like(do)
+    doz[q_pos0:] = do[q_pos0:]
+    sels_b = [[[list(map(int, s_)) for s_ in row] for row in r["sel"][cc]] for cc in range(c + 1)]
+    b = attn_brute(q.tolist(), k.tolist(), v.tolist(), doz.tolist(), chunk, scale, page, sels_b)
+    bk, bv = np.array(b[3]), np.array(b[4])
+    for j in pages:
+        m = min(page, n - j * page)
+        assert np.abs(dk[j, :m] - bk[j * page:j * page + m]).max() < 1e-11
+        assert np.abs(dv[j, :m] - bv[j * page:j * page + m]).max() < 1e-11
+        assert np.abs(dk[j, m:]).max(initial=0.0) == 0.0 and np.abs(dv[j, m:]).max(initial=0.0) == 0.0
