@@ -306,9 +306,10 @@ pkv_status pkv_select_topk_pages(pkv_pool* pool, int32_t layer, int64_t q_pos0, 
  * instead zeroes them in the window, on the stream of the layer's first
  * attention backward (or writeback) after the prefetch.  The window slot
  * the layer lands in is not overwritten before earlier attention calls that
- * read it have finished, nor its gradients before the window's previous
- * pkv_writeback_grads has read them (the library orders this with events;
- * that writeback must have been called before this prefetch).  `ready`, if
+ * read it and the slot's previous fetch (on any copy stream) have finished,
+ * nor its gradients before the window's previous pkv_writeback_grads has
+ * read them (the library orders this with events; that writeback must have
+ * been called before this prefetch).  `ready`, if
  * not NULL, is recorded on copy_stream when the copies are done; attention
  * calls on this layer wait for it on their own stream automatically.
  * The window then covers the keys appended so far: attention calls on the
@@ -368,7 +369,8 @@ pkv_status pkv_writeback_grads(pkv_pool* pool, int32_t layer, hipStream_t copy_s
 pkv_status pkv_offload_bytes(pkv_pool* pool, int64_t* fetched, int64_t* written);
 
 /* Zero the dK/dV pool of `layer` (all slots; the host tier too in host-tier
- * mode, synchronously, after any pending host adds).  (Support call: the
+ * mode, synchronously, after all work on the device, pending writebacks
+ * included, and any pending host adds).  (Support call: the
  * gradient pool accumulates in place over the chunks of a training step, de
  * 2.B; a new step starts it from zero.) */
 pkv_status pkv_grad_zero(pkv_pool* pool, int32_t layer, hipStream_t stream);

@@ -309,6 +309,10 @@ pkv_status pool_grad_zero(pkv_pool* p, int layer, hipStream_t s) {
       return pool_hip_fail(e, "pkv_grad_zero");
     return PKV_OK;
   }
+  // every transfer first: a writeback still in flight on a copy stream (or
+  // an attention backward adding into the window) would otherwise land after
+  // the zeros
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return pool_hip_fail(e, "pkv_grad_zero: sync");
   pkv_status st = pool_host_adds_wait(p);
   if (st != PKV_OK) return st;
   const int64_t hgr = p->layer_elems * grad_host_bytes(p);
@@ -420,9 +424,15 @@ pkv_status pool_prefetch(pkv_pool* p, int layer, const pkv_sel* sel, int64_t n_k
   p->window_keys[w] = 0;
   p->zero_pending[w] = false;
   // K/V of the window are free once the attention calls on its last layer ran
+  // and the window's previous fetch (possibly on another copy stream, and
+  // possibly never used) has finished writing it
   if (p->compute_recorded[w]) {
     if ((e = hipStreamWaitEvent(cs, p->ev_compute[w], 0)) != hipSuccess)
       return pool_hip_fail(e, "hipStreamWaitEvent (window reuse)");
+  }
+  if (p->ready_recorded[w]) {
+    if ((e = hipStreamWaitEvent(cs, p->ev_ready[w], 0)) != hipSuccess)
+      return pool_hip_fail(e, "hipStreamWaitEvent (window's previous fetch)");
   }
   // build the other list buffer, once the writeback that last read it ran
   const int b = p->list_gen[w] ^ 1;

@@ -358,6 +358,76 @@ def test_failed_transfers_leave_a_consistent_pool(accumulate):
         assert rel_err(failed[name], ok[name]) < 1e-5, name
 
 
+@pytest.mark.parametrize("accumulate", [0, 1])
+def test_copy_streams_and_grad_zero_are_ordered(accumulate):
+    """Two prefetches into one window slot issued on two different copy
+    streams (layers 0 and 2 share window 0; the first prefetch is never
+    used): the second waits for the first's copies, so the window ends up
+    holding layer 2 alone and attention on it gives what the same calls on
+    one copy stream give (O, LSE, dQ bit-identical; dK/dV within fp32
+    summation-order noise, fp32 host gradients).  Then a writeback on one
+    copy stream followed at once by pkv_grad_zero on another: the zeroing
+    waits for the writeback (and the host adds), so the layer's gradients
+    read back as zeros."""
+    import torch
+    import paged_kv_cache_chunk_amd as pkv
+    cfg = CFG  # 3 layers
+    ws = {l: Workload(cfg, layer=l) for l in (0, 2)}
+    dev = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    last = ws[2].chunk(cfg.n_chunks - 1)
+    n_keys = last.q_pos0 + last.n_q
+
+    def run(two_streams):
+        pool = pkv.pkv_pool_create(3, cfg.hkv, cfg.d, cfg.page, cfg.n_pages, cfg.slots,
+                                   pkv.PKV_BF16, host_tier=1, host_grad_dtype=pkv.PKV_F32,
+                                   host_grad_accumulate=accumulate)
+        for l, w in ws.items():
+            tab = w.table()
+            for g in range(cfg.hkv):
+                pkv.pkv_page_table_set(pool, l, g, tab[g])
+            for c in range(cfg.n_chunks):
+                ch = w.chunk(c)
+                pkv.pkv_append_kv(pool, l, ch.q_pos0, dev(ch.k), dev(ch.v))
+        torch.cuda.synchronize()
+        s1 = torch.cuda.Stream()
+        s2 = torch.cuda.Stream() if two_streams else s1
+        q, do = dev(last.q), dev(last.do)
+        o = torch.empty_like(q)
+        lse = torch.empty(cfg.hq, last.n_q, device="cuda")
+        dq = torch.empty(last.n_q, cfg.hq, cfg.d, device="cuda")
+        pkv.pkv_prefetch_pages(pool, 0, None, with_grads=True, copy_stream=s1)
+        pkv.pkv_prefetch_prefix(pool, 2, n_keys, with_grads=True, copy_stream=s2)
+        pkv.pkv_attn_fwd(pool, 2, last.q_pos0, q, o, lse, cfg.scale)
+        pkv.pkv_attn_bwd(pool, 2, last.q_pos0, q, o, do, lse, dq, cfg.scale)
+        pkv.pkv_writeback_grads(pool, 2, copy_stream=s1)
+        dk = torch.empty(cfg.n_ctx, cfg.hkv, cfg.d, dtype=torch.float32, device="cuda")
+        dv = torch.empty_like(dk)
+        pkv.pkv_read_pages(pool, 2, pkv.PKV_DK, dk)
+        pkv.pkv_read_pages(pool, 2, pkv.PKV_DV, dv)
+        torch.cuda.synchronize()
+        out = dict(O=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.cpu().numpy(),
+                   dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
+        # a second visit's writeback, then the zeroing on the other stream
+        pkv.pkv_prefetch_prefix(pool, 2, n_keys, with_grads=True, copy_stream=s2)
+        pkv.pkv_attn_bwd(pool, 2, last.q_pos0, q, o, do, lse, dq, cfg.scale)
+        pkv.pkv_writeback_grads(pool, 2, copy_stream=s1)
+        pkv.pkv_grad_zero(pool, 2, stream=s2)
+        pkv.pkv_read_pages(pool, 2, pkv.PKV_DK, dk)
+        pkv.pkv_read_pages(pool, 2, pkv.PKV_DV, dv)
+        torch.cuda.synchronize()
+        out["zeroed"] = float(max(dk.abs().max().item(), dv.abs().max().item()))
+        pool.close()
+        return out
+
+    one, two = run(False), run(True)
+    for name in ("O", "lse", "dq"):
+        assert np.array_equal(two[name], one[name]), name
+    for name in ("dk", "dv"):
+        assert np.abs(one[name]).max() > 0
+        assert rel_err(two[name], one[name]) < 1e-5, name
+    assert one["zeroed"] == 0.0 and two["zeroed"] == 0.0
+
+
 # 64 pages per layer, chunks of 4 query pages, top-K 6 + 3 forced: a visit
 # names at most 4 x 9 = 36 pages per KV head, so a window of 36 slots per head
 # holds any selection while a layer has 64 pages
