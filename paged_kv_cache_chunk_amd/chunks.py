@@ -13,8 +13,7 @@ from typing import Optional
 
 import torch
 
-from . import (PKV_BF16, PKV_F32, Pool, pkv_append_kv, pkv_attn_bwd, pkv_attn_fwd,
-               pkv_select_topk_pages)
+from . import PKV_BF16, Pool, pkv_attn_bwd, pkv_attn_fwd, pkv_select_topk_pages
 
 
 def torch_dtype(kv_dtype: int) -> torch.dtype:

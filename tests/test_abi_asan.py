@@ -9,7 +9,6 @@ suppressed)."""
 import concurrent.futures
 import glob
 import os
-import shutil
 import subprocess
 
 import pytest
