@@ -111,14 +111,19 @@ __device__ __forceinline__ float4 hi4(uint4 a) {
                      __uint_as_float(a.w << 16), __uint_as_float(a.w & 0xffff0000u));
 }
 
-// A small persistent grid (kCopyBlocks workgroups) does the host-link copies,
-// so that they occupy a few CUs next to the attention kernels instead of
-// flooding the whole GPU.  Each workgroup copies whole page-heads from the
-// list (its next list entry loaded one page-head ahead).  Host-mapped memory
-// answers after microseconds, so a workgroup's bandwidth is its bytes in
-// flight over that latency: every thread keeps kInflight 16-byte loads in
-// flight.  (A flat stream of 16-byte units over all listed page-heads was
-// slower on the host link: 38 vs 42 GB/s host -> HBM, 41 vs 50 back.)
+// A small persistent grid does the host-link copies (kFetchBlocks workgroups
+// host -> HBM, kCopyBlocks HBM -> host), so that they occupy a few CUs next to
+// the attention kernels instead of flooding the whole GPU.  Each workgroup
+// copies whole page-heads from the list (its next list entry loaded one
+// page-head ahead).  Host-mapped memory answers after microseconds, so a
+// workgroup's bandwidth is its bytes in flight over that latency: every thread
+// keeps kInflight 16-byte loads in flight.  (A flat stream of 16-byte units
+// over all listed page-heads was slower on the host link: 38 vs 42 GB/s host
+// -> HBM, 41 vs 50 back.)  The fetch's grid is sized against a writeback made
+// by the DMA engines at the same time: on the 1M-token top-K stack, 24 fetch
+// workgroups reach ~39 GB/s, 32 reach ~48 GB/s with the writeback still at
+// ~48 GB/s, and 36 or 40 take the writeback down to 36-41 GB/s.
+constexpr int kFetchBlocks = 32;
 constexpr int kCopyBlocks = 24;
 constexpr int kInflight = 8;
 
@@ -424,7 +429,7 @@ hipError_t launch_fetch(const pkv_pool* p, int layer, int window, hipStream_t s,
   const WindowList L = window_list(p, window);
   const int grad_mode = with_grads ? (d.host_grad_dtype == PKV_BF16 ? 1 : 2) : 0;
   KernelTimer t(KT_FETCH, s);
-  hipLaunchKernelGGL(fetch_kernel, dim3(kCopyBlocks), dim3(256), 0, s, L.items, L.count,
+  hipLaunchKernelGGL(fetch_kernel, dim3(kFetchBlocks), dim3(256), 0, s, L.items, L.count,
                      (int64_t)d.page_size * d.head_dim, true, p->kv_bytes,
                      (const char*)p->m_k[layer], (const char*)p->m_v[layer],
                      (char*)p->d_k + window * p->dev_elems * p->kv_bytes,
