@@ -194,7 +194,9 @@ pkv_status pkv_pool_destroy(pkv_pool* pool);
 pkv_status pkv_page_table_set(pkv_pool* pool, int32_t layer, int32_t kv_head,
                               const int32_t* host_slots, int32_t n);
 
-/* Number of tokens appended so far to `layer` (host value; -1 on bad args). */
+/* Number of tokens appended so far to `layer` (host value; -1 on bad args).
+ * (Support call: the chunk-recurrent driver appends one chunk after another,
+ * de 2.A, and takes the next chunk's first position from here.) */
 int64_t pkv_length(const pkv_pool* pool, int32_t layer);
 
 /* Append n_tok tokens at positions [pos0, pos0 + n_tok) to `layer`:
@@ -412,10 +414,13 @@ pkv_status pkv_read_rows(pkv_pool* pool, int32_t layer, int32_t what, int64_t po
 /* Forget the tokens of `layer` (length back to 0) so that a new sequence can
  * be appended; no memory is freed or cleared (gradients are left as they
  * are: pkv_grad_zero clears them; a host-tier window holding the layer then
- * covers no keys until the next prefetch).  Host-only, immediate. */
+ * covers no keys until the next prefetch).  Host-only, immediate.  (Support
+ * call: the pages are allocated once and reused, de 2.B; a new training
+ * sequence reuses them.) */
 pkv_status pkv_pool_reset(pkv_pool* pool, int32_t layer);
 
-/* Kernel timing.  While enabled, every kernel the library launches is
+/* Kernel timing (measurement support: the per-kernel times behind the
+ * rates of the hot path's steps, de 2.B and 2.D).  While enabled, every kernel the library launches is
  * bracketed by two HIP events recorded on the stream it is launched on, and
  * its duration is added to the counter of its kind.  Kinds: */
 typedef enum {
@@ -440,7 +445,10 @@ pkv_status pkv_kernel_timing(int32_t enable);
  * launches[k] for k < n (n <= PKV_KT_COUNT).  Either array may be NULL. */
 pkv_status pkv_kernel_times(int32_t n, double* total_ms, int64_t* launches);
 
-/* Bytes the pool holds on the device and in pinned host memory. */
+/* Bytes the pool holds on the device and in pinned host memory.
+ * (Measurement support: the pool's footprint is exactly its page bytes,
+ * sciencestack Figure 4, and its HBM side bounds the memory growth per
+ * context length that de 4 reports.) */
 pkv_status pkv_pool_bytes(const pkv_pool* pool, int64_t* device_bytes, int64_t* host_bytes);
 
 /* ---- Measurement kernels (not used by the attention path).  They move the
@@ -469,7 +477,8 @@ pkv_status pkv_measure_gather(pkv_pool* pool, int32_t layer, int64_t q_pos0, int
 pkv_status pkv_measure_atomics(pkv_pool* pool, int32_t layer, int64_t n_keys, int32_t reps,
                                float value, hipStream_t stream);
 
-/* Thread-local message of the last non-OK status returned on this thread. */
+/* Thread-local message of the last non-OK status returned on this thread
+ * (support call: error reporting of the interface, see Errors above). */
 const char* pkv_last_error(void);
 
 #ifdef __cplusplus
